@@ -1,0 +1,15 @@
+"""Float64 CPU oracle (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this package; the library never does.
+"""
+from .swa_oracle import (  # noqa: F401
+    allowed_set,
+    allowed_mask,
+    allowed_pair_count,
+    attn_fwd,
+    attn_fwd_rows,
+    attn_fwd_parallel,
+    decode,
+    ring_slot,
+)

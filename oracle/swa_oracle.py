@@ -1,0 +1,285 @@
+"""Float64 CPU oracle for causal sliding-window attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run anything in this folder.
+The library under ``sparse_causal_attention_band_amd/`` never imports it, and
+this module imports nothing from there: the two share no code.
+
+Everything here is the plain definition, written out in float64 with numpy:
+
+* The allowed key set of a query row follows the window definition of the page
+  "SWA：滑动窗口注意力与跨层信息传递" (§3.1, the set N_W(i) and the mask
+  M^SWA): row i may read key j iff max(1, i-W+1) <= j <= i in that page's
+  1-based numbering, i.e. the window W counts the current position.  Here
+  positions are 0-based, so the band is [max(0, i-W+1), i], which is also the
+  range used by the sliding-window mask of the page
+  "注意力变体——滑动窗口、稀疏、差分" (构建它, 第 2 步).
+* The local + strided variant adds, to that band, every key j <= i with
+  j mod stride == 0 (0-based j), as in the same page's step 3 ("局部 + 步进
+  稀疏掩码"); the union is a set, a key is counted once.  stride <= 0 means no
+  strided part.
+* Attention is softmax(scale * Q K^T + M) V with the softmax taken row by row,
+  so each query normalises over its own allowed keys only (SWA page, §3.1;
+  the scale is 1/sqrt(d_k) there and is an explicit argument here).
+* The rolling decode cache stores absolute position t (1-based) in slot
+  (t-1) mod W (SWA page, §4.2); slot order is not time order, so the oracle
+  gathers the valid slots back into time order before attending.
+
+Readings where the pages leave a step open (each one is also listed in the
+design notes of the repository):
+
+* grouped query heads: query head h reads KV head h // (Hq // Hkv);
+* decode ``pos[b]`` is the 1-based absolute position of the one query token,
+  whose own K/V are already in the ring; it attends to the min(pos, W) most
+  recent positions; pos <= 0 yields an all-zero output row;
+* the oracle subtracts the row maximum before exponentiating (same value
+  mathematically); every row has at least its own key, so no row is empty.
+
+Query rows are processed in blocks only to bound memory: each row's softmax is
+still taken over exactly its own allowed set (keys outside the union of the
+block's allowed sets have weight exp(-inf) = 0 and are simply not gathered).
+"""
+from __future__ import annotations
+
+import os
+from typing import Iterable, Optional
+
+import numpy as np
+
+__all__ = [
+    "allowed_set",
+    "allowed_mask",
+    "allowed_pair_count",
+    "attn_fwd",
+    "attn_fwd_rows",
+    "decode",
+    "ring_slot",
+    "attn_fwd_parallel",
+]
+
+
+def allowed_set(i: int, window: int, stride: int = 0) -> list[int]:
+    """Sorted allowed key positions of 0-based query row ``i``.
+
+    Band: [max(0, i-W+1), i] (SWA page §3.1, 0-based).  Strided part: every
+    j in 0, stride, 2*stride, ... that is <= i (attention-variants page, step 3).
+    """
+    if window < 1:
+        raise ValueError("window must be >= 1")
+    lo = max(0, i - window + 1)
+    keys = set(range(lo, i + 1))
+    if stride > 0:
+        keys.update(range(0, i + 1, stride))
+    return sorted(keys)
+
+
+def allowed_mask(n: int, window: int, stride: int = 0) -> np.ndarray:
+    """Boolean n x n matrix, True where (row i, key j) is allowed.
+
+    Built row by row from ``allowed_set``; used for small n only.
+    """
+    m = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        m[i, allowed_set(i, window, stride)] = True
+    return m
+
+
+def allowed_pair_count(n: int, window: int, stride: int = 0) -> int:
+    """Total number of allowed (query, key) pairs, summed over rows.
+
+    Counted from the row sets themselves (no closed form here; the closed
+    forms live in the tests, where they pin this function).
+    """
+    total = 0
+    for i in range(n):
+        lo = max(0, i - window + 1)
+        band = i - lo + 1
+        extra = 0
+        if stride > 0 and lo > 0:
+            # multiples of stride strictly below the band start (those inside
+            # the band are already counted once)
+            extra = (lo - 1) // stride + 1
+        total += band + extra
+    return total
+
+
+def _block_keys(i0: int, i1: int, window: int, stride: int) -> np.ndarray:
+    """Union of the allowed sets of rows i0..i1 (inclusive), sorted."""
+    lo = max(0, i0 - window + 1)
+    keys = list(range(lo, i1 + 1))
+    if stride > 0:
+        keys = sorted(set(keys).union(range(0, i1 + 1, stride)))
+    return np.asarray(keys, dtype=np.int64)
+
+
+def _row_allowed(rows: np.ndarray, keys: np.ndarray, window: int, stride: int) -> np.ndarray:
+    """Boolean [len(rows), len(keys)]: the definition, evaluated elementwise."""
+    i = rows[:, None]
+    j = keys[None, :]
+    in_band = (j <= i) & (j >= np.maximum(0, i - window + 1))
+    if stride > 0:
+        in_stride = (j <= i) & (j % stride == 0)
+        return in_band | in_stride
+    return in_band
+
+
+def _masked_softmax_rows(scores: np.ndarray, allowed: np.ndarray) -> np.ndarray:
+    """Row-wise softmax over the allowed entries only (float64)."""
+    s = np.where(allowed, scores, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.where(allowed, np.exp(s - m), 0.0)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def _head_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.ndarray,
+               window: int, stride: int, scale: float) -> np.ndarray:
+    """Output rows ``rows`` of one (batch, head): q [N,d], k/v [N,d] float64."""
+    out = np.empty((len(rows), v.shape[1]), dtype=np.float64)
+    if len(rows) == 0:
+        return out
+    # group consecutive rows so a block shares one gathered key list
+    block = 256
+    start = 0
+    while start < len(rows):
+        stop = start + 1
+        while stop < len(rows) and stop - start < block and rows[stop] == rows[stop - 1] + 1:
+            stop += 1
+        r = rows[start:stop]
+        keys = _block_keys(int(r[0]), int(r[-1]), window, stride)
+        scores = scale * (q[r] @ k[keys].T)
+        p = _masked_softmax_rows(scores, _row_allowed(r, keys, window, stride))
+        out[start:stop] = p @ v[keys]
+        start = stop
+    return out
+
+
+def _check(q, k, v, window):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, N, d] matching q")
+    if Hq % k.shape[1] != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if window < 1:
+        raise ValueError("window must be >= 1")
+
+
+def attn_fwd_rows(q, k, v, window: int, stride: int, scale: float,
+                  bh_rows: Iterable[tuple[int, int, int]]) -> np.ndarray:
+    """Selected output rows: one float64 [d] vector per (b, h, i) triple."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    _check(q, k, v, window)
+    G = q.shape[1] // k.shape[1]
+    res = []
+    for b, h, i in bh_rows:
+        res.append(_head_rows(q[b, h], k[b, h // G], v[b, h // G],
+                              np.asarray([i], dtype=np.int64), window, stride, scale)[0])
+    return np.stack(res) if res else np.zeros((0, q.shape[3]))
+
+
+def attn_fwd(q, k, v, window: int, stride: int = 0, scale: Optional[float] = None) -> np.ndarray:
+    """Full forward: float64 [B, Hq, N, d].
+
+    q: [B, Hq, N, d], k/v: [B, Hkv, N, d]; any real dtype, converted exactly
+    to float64.  ``scale`` defaults to 1/sqrt(d) (SWA page §3.1).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    _check(q, k, v, window)
+    B, Hq, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    G = Hq // k.shape[1]
+    out = np.empty((B, Hq, N, v.shape[3]), dtype=np.float64)
+    rows = np.arange(N, dtype=np.int64)
+    for b in range(B):
+        for h in range(Hq):
+            out[b, h] = _head_rows(q[b, h], k[b, h // G], v[b, h // G], rows, window, stride, scale)
+    return out
+
+
+def _pool_job(args):
+    q, k, v, rows, window, stride, scale = args
+    return _head_rows(q, k, v, rows, window, stride, scale)
+
+
+def attn_fwd_parallel(q, k, v, window: int, stride: int, scale: float,
+                      rows: np.ndarray, workers: Optional[int] = None):
+    """Same arithmetic as ``attn_fwd`` for the given query rows of every
+    (b, h), spread over a process pool (one (b, h) per task, one BLAS thread
+    per worker).  Returns (float64 [B, Hq, len(rows), d], workers used)."""
+    import multiprocessing as mp
+
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    _check(q, k, v, window)
+    B, Hq, N, d = q.shape
+    G = Hq // k.shape[1]
+    if workers is None:
+        workers = len(os.sched_getaffinity(0))
+    rows = np.asarray(rows, dtype=np.int64)
+    jobs = [(q[b, h], k[b, h // G], v[b, h // G], rows, window, stride, scale)
+            for b in range(B) for h in range(Hq)]
+    env_keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {kk: os.environ.get(kk) for kk in env_keys}
+    for kk in env_keys:
+        os.environ[kk] = "1"
+    try:
+        ctx = mp.get_context("fork")
+        with ctx.Pool(workers) as pool:
+            parts = pool.map(_pool_job, jobs, chunksize=1)
+    finally:
+        for kk, val in saved.items():
+            if val is None:
+                os.environ.pop(kk, None)
+            else:
+                os.environ[kk] = val
+    out = np.stack(parts).reshape(B, Hq, len(rows), d)
+    return out, workers
+
+
+def ring_slot(t: int, window: int) -> int:
+    """Ring slot holding 1-based absolute position t (SWA page §4.2)."""
+    return (t - 1) % window
+
+
+def decode(q, kring, vring, pos, window: int, scale: Optional[float] = None) -> np.ndarray:
+    """One decode step per sequence over a rolling W-slot cache, float64.
+
+    q: [B, Hq, d]; kring, vring: [B, Hkv, W, d]; pos: [B] 1-based absolute
+    positions of the query tokens.  The query attends to positions
+    pos-n+1 .. pos with n = min(pos, W), read from slots (t-1) mod W and put
+    back into time order; pos <= 0 gives zeros.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kring = np.asarray(kring, dtype=np.float64)
+    vring = np.asarray(vring, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    B, Hq, d = q.shape
+    if kring.shape[2] != window or vring.shape != kring.shape:
+        raise ValueError("rings must be [B, Hkv, W, d]")
+    if Hq % kring.shape[1] != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    G = Hq // kring.shape[1]
+    out = np.zeros((B, Hq, vring.shape[3]), dtype=np.float64)
+    for b in range(B):
+        p = int(pos[b])
+        if p <= 0:
+            continue
+        n = min(p, window)
+        times = range(p - n + 1, p + 1)
+        slots = np.asarray([ring_slot(t, window) for t in times], dtype=np.int64)
+        for h in range(Hq):
+            kk = kring[b, h // G][slots]
+            vv = vring[b, h // G][slots]
+            s = scale * (kk @ q[b, h])
+            e = np.exp(s - s.max())
+            out[b, h] = (e / e.sum()) @ vv
+    return out
