@@ -1,0 +1,121 @@
+/*
+ * swa_attn.h -- C ABI of the MI355X (gfx950) sliding-window attention library.
+ *
+ * What is computed
+ * ----------------
+ * Causal sliding-window attention, softmax(scale * Q K^T + M) V, taken row by
+ * row: query position i (0-based) reads key j iff
+ *     j <= i  and  ( i - j < window   or   (stride > 0 and j % stride == 0) ).
+ * The window counts the current position: with window W the band is
+ * [max(0, i-W+1), i].  This is the set N_W(i) and mask M^SWA of the page
+ * "SWA：滑动窗口注意力与跨层信息传递" (§3.1), written 0-based; the strided
+ * part is the "local + strided" mask of the page
+ * "注意力变体——滑动窗口、稀疏、差分" (构建它, 第 3 步), whose union with the
+ * band is a set (a key is read once).  window >= N is full causal attention,
+ * window == 1 returns V row for row.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees or synchronises: each call validates its
+ *    arguments on the host, enqueues its kernels on `stream` (NULL = the
+ *    default stream) and returns.  Results are ready when the stream reaches
+ *    that point.
+ *  - Tensors are dense, row-major, with no padding between rows.
+ *  - "bf16" is bfloat16 stored as 16-bit words.  Arithmetic is fp32 inside
+ *    (scores, softmax and accumulators); the probabilities are rounded to
+ *    bf16 (round to nearest even) for the P*V product on the bf16 matrix
+ *    cores, the output is rounded once to bf16.  The *_f32 entry points do
+ *    every step in fp32.
+ *  - Grouped heads: query head h reads KV head h / (Hq / Hkv).
+ *  - Return value: SWA_OK, or a negative code; on error nothing has been
+ *    enqueued and swa_last_error() describes the problem.  No entry point
+ *    aborts or throws.  Device-side data (decode `pos`) is not validated.
+ *  - Outputs are deterministic: fixed reduction order, no float atomics.
+ *  - Calls on different streams may run concurrently; a workspace must not be
+ *    shared by calls that may overlap.
+ */
+#ifndef SWA_ATTN_H
+#define SWA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifndef SWA_API
+#define SWA_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SWA_OK = 0,
+    SWA_ERR_INVALID_ARG = -1, /* bad size, null or misaligned pointer, small workspace */
+    SWA_ERR_UNSUPPORTED = -2, /* valid but not built: head dim other than 64/128, ... */
+    SWA_ERR_HIP = -3          /* a HIP launch failed; message from hipGetErrorString */
+};
+
+/*
+ * Prefill / whole-sequence forward, bf16 in, bf16 out.
+ *   q, out : [B, Hq, N, d]     k, v : [B, Hkv, N, d]
+ *   B, N >= 1; Hq % Hkv == 0; d in {64, 128}; window >= 1 (values >= N are
+ *   treated as N: full causal, same bits); stride <= 0 disables the strided
+ *   part; scale is any finite non-zero float (1/sqrt(d) for the usual
+ *   attention).  Every pointer must be 16-byte aligned.  out must not alias
+ *   q, k or v.
+ * The band kernel visits only the (query tile, key tile) pairs that meet
+ * the band (plus, when stride > 0, a compact tile list of the strided keys
+ * below the band), so fully masked tiles are never loaded.
+ */
+SWA_API int swa_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                 int B, int Hq, int Hkv, int N, int d,
+                 int window, int stride, float scale, hipStream_t stream);
+
+/* Same contract with fp32 tensors and fp32 matrix-core arithmetic. */
+SWA_API int swa_attn_fwd_f32(const float* q, const float* k, const float* v, float* out,
+                     int B, int Hq, int Hkv, int N, int d,
+                     int window, int stride, float scale, hipStream_t stream);
+
+/*
+ * One decode step per sequence over a rolling window-slot KV cache.
+ * Absolute position t (1-based) lives in ring slot (t-1) % window, the rule
+ * of the SWA page (§4.2); slot order is not time order, and since the
+ * attention itself has no positional term the step reduces over the valid
+ * slots in slot order.
+ *   q, out       : [B, Hq, d]           (bf16)
+ *   kring, vring : [B, Hkv, window, d]  (bf16)
+ *   pos          : int32 [B] on the device: 1-based absolute position of each
+ *                  query token, whose own K/V are already in the ring.  The
+ *                  step reads n = min(pos, window) slots: all of them once
+ *                  pos >= window, else slots 0 .. pos-1.  pos <= 0 gives an
+ *                  all-zero output row.  Unread slots may hold anything,
+ *                  NaN included.
+ *   workspace    : device scratch of at least
+ *                  swa_decode_workspace_bytes(B, Hq, Hkv, d, window) bytes,
+ *                  16-byte aligned; its contents on entry do not matter.
+ *   Hq / Hkv must be 1, 2, 4 or 8; d in {64, 128}; window >= 1.
+ * Two kernels run: a split-K pass that streams K/V slots from HBM and writes
+ * per-split (max, sum, weighted V) partials into the workspace, then a
+ * log-sum-exp merge of the splits that writes `out`.
+ */
+SWA_API int swa_decode(const void* q, const void* kring, const void* vring, const int32_t* pos,
+               void* out, int B, int Hq, int Hkv, int d, float scale,
+               void* workspace, size_t workspace_bytes, int window, hipStream_t stream);
+
+/* Same contract with fp32 q, rings and out. */
+SWA_API int swa_decode_f32(const float* q, const float* kring, const float* vring, const int32_t* pos,
+                   float* out, int B, int Hq, int Hkv, int d, float scale,
+                   void* workspace, size_t workspace_bytes, int window, hipStream_t stream);
+
+/* Workspace bytes swa_decode / swa_decode_f32 need; 0 for invalid sizes. */
+SWA_API size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window);
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+SWA_API const char* swa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SWA_ATTN_H */

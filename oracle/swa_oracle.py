@@ -146,9 +146,12 @@ def _head_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.ndarray,
             stop += 1
         r = rows[start:stop]
         keys = _block_keys(int(r[0]), int(r[-1]), window, stride)
-        scores = scale * (q[r] @ k[keys].T)
+        qr = np.asarray(q[r], dtype=np.float64)
+        kk = np.asarray(k[keys], dtype=np.float64)
+        vv = np.asarray(v[keys], dtype=np.float64)
+        scores = scale * (qr @ kk.T)
         p = _masked_softmax_rows(scores, _row_allowed(r, keys, window, stride))
-        out[start:stop] = p @ v[keys]
+        out[start:stop] = p @ vv
         start = stop
     return out
 
@@ -167,10 +170,12 @@ def _check(q, k, v, window):
 
 def attn_fwd_rows(q, k, v, window: int, stride: int, scale: float,
                   bh_rows: Iterable[tuple[int, int, int]]) -> np.ndarray:
-    """Selected output rows: one float64 [d] vector per (b, h, i) triple."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
+    """Selected output rows: one float64 [d] vector per (b, h, i) triple.
+
+    Inputs may be any real numpy dtype (e.g. float32 holding bf16 values);
+    only the rows each triple needs are converted to float64.
+    """
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
     _check(q, k, v, window)
     G = q.shape[1] // k.shape[1]
     res = []

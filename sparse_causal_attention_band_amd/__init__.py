@@ -1,0 +1,16 @@
+"""Causal sliding-window attention for MI355X (gfx950).
+
+Python face of ``libswa_attn.so``: ``attn_fwd`` (band + optional strided
+keys, whole-sequence forward) and ``decode`` (one token per sequence over a
+rolling window-slot KV cache).  The arithmetic runs in hand-written HIP
+kernels behind the C ABI declared in ``include/swa_attn.h``.
+"""
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    SIGNATURES,
+    SwaError,
+    attn_fwd,
+    decode,
+    decode_workspace_bytes,
+    lib,
+)

@@ -1,0 +1,162 @@
+"""ctypes binding of ``libswa_attn.so`` (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module
+checks tensor dtype/shape/device on the Python side, allocates outputs with
+torch (device memory), passes raw pointers and the current HIP stream, and
+turns a non-zero return code into an exception.  There is no fallback: if
+the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loads the HIP runtime first, so the library binds to that same runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libswa_attn.so")
+
+SWA_OK = 0
+SWA_ERR_INVALID_ARG = -1
+SWA_ERR_UNSUPPORTED = -2
+SWA_ERR_HIP = -3
+
+# name -> (restype, argtypes); mirrors include/swa_attn.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_Z = ctypes.c_size_t
+SIGNATURES = {
+    "swa_attn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "swa_attn_fwd_f32": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "swa_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _Z, _I, _P]),
+    "swa_decode_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _Z, _I, _P]),
+    "swa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "swa_last_error": (ctypes.c_char_p, []),
+}
+
+
+class SwaError(RuntimeError):
+    """A library entry point returned a non-zero code."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the shared library (once); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                "or `python sparse_causal_attention_band_amd/build.py` first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != SWA_OK:
+        raise SwaError(rc, lib().swa_last_error().decode())
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: int, stride: int = 0,
+             scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal sliding-window (optionally + strided) attention forward.
+
+    q: [B, Hq, N, d], k/v: [B, Hkv, N, d], all bf16 (or all fp32) on one GPU.
+    Returns out [B, Hq, N, d] in the input dtype.  scale defaults to 1/sqrt(d).
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    dtype, dev = q.dtype, q.device
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bfloat16 or float32")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dtype, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    fn = lib().swa_attn_fwd if dtype == torch.bfloat16 else lib().swa_attn_fwd_f32
+    _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, k.shape[1], N, d,
+              int(window), int(stride), float(scale), _stream(dev)))
+    return out
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, window: int) -> int:
+    return int(lib().swa_decode_workspace_bytes(B, Hq, Hkv, d, window))
+
+
+def decode(q: torch.Tensor, kring: torch.Tensor, vring: torch.Tensor, pos: torch.Tensor,
+           scale: float | None = None, out: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step over a rolling window-slot cache.
+
+    q: [B, Hq, d]; kring/vring: [B, Hkv, W, d] (window W = kring.shape[2]);
+    pos: int32 [B] on the GPU, 1-based absolute position of each query token.
+    """
+    if q.dim() != 3 or kring.dim() != 4 or vring.shape != kring.shape:
+        raise ValueError("q must be [B, Hq, d] and kring/vring [B, Hkv, W, d]")
+    B, Hq, d = q.shape
+    W = kring.shape[2]
+    if kring.shape[0] != B or kring.shape[3] != d:
+        raise ValueError("ring shape does not match q")
+    dtype, dev = q.dtype, q.device
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bfloat16 or float32")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    for t, n in ((q, "q"), (kring, "kring"), (vring, "vring")):
+        _need(t, n, dtype, dev)
+    _need(pos, "pos", torch.int32, dev)
+    if pos.shape != (B,):
+        raise ValueError("pos must be [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype, dev)
+    need = decode_workspace_bytes(B, Hq, kring.shape[1], d, W)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the same GPU")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    fn = lib().swa_decode if dtype == torch.bfloat16 else lib().swa_decode_f32
+    _check(fn(q.data_ptr(), kring.data_ptr(), vring.data_ptr(), pos.data_ptr(), out.data_ptr(),
+              B, Hq, kring.shape[1], d, float(scale), workspace.data_ptr(),
+              workspace.numel() * workspace.element_size(), W, _stream(dev)))
+    return out

@@ -1,0 +1,172 @@
+// C ABI of the library: argument validation on the host, launch geometry,
+// error reporting.  Declared in include/swa_attn.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string>
+
+#include "swa_attn.h"
+#include "swa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return SWA_OK;
+}
+
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+int check_scale(const char* name, float scale) {
+    if (!isfinite(scale) || scale == 0.f)
+        return fail(SWA_ERR_INVALID_ARG, "%s: scale must be finite and non-zero (got %g)", name, (double)scale);
+    return SWA_OK;
+}
+
+int attn_fwd(bool bf16, const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N,
+             int d, int window, int stride, float scale, hipStream_t stream) {
+    const char* name = bf16 ? "swa_attn_fwd" : "swa_attn_fwd_f32";
+    if (B < 1 || N < 1 || Hq < 1 || Hkv < 1)
+        return fail(SWA_ERR_INVALID_ARG, "%s: B, N, Hq, Hkv must be >= 1 (B=%d N=%d Hq=%d Hkv=%d)", name, B, N, Hq,
+                    Hkv);
+    if (Hq % Hkv != 0) return fail(SWA_ERR_INVALID_ARG, "%s: Hq (%d) must be a multiple of Hkv (%d)", name, Hq, Hkv);
+    if (window < 1) return fail(SWA_ERR_INVALID_ARG, "%s: window must be >= 1 (got %d)", name, window);
+    if (d != 64 && d != 128) return fail(SWA_ERR_UNSUPPORTED, "%s: head dim %d not built (64 or 128)", name, d);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(SWA_ERR_INVALID_ARG, "%s: q, k, v, out must be non-null and 16-byte aligned", name);
+    if (int rc = check_scale(name, scale)) return rc;
+    const long long es = bf16 ? 2 : 4;
+    const long long qbytes = (long long)B * Hq * N * d * es;
+    const long long kbytes = (long long)B * Hkv * N * d * es;
+    auto overlap = [](const void* a, long long na, const void* b, long long nb) {
+        const char* x = (const char*)a;
+        const char* y = (const char*)b;
+        return x < y + nb && y < x + na;
+    };
+    if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k, kbytes) || overlap(out, qbytes, v, kbytes))
+        return fail(SWA_ERR_INVALID_ARG, "%s: out must not overlap q, k or v", name);
+    const long long G = Hq / Hkv;
+    const long long rows = (long long)N * d;
+    if ((long long)B * Hq * rows > (1ll << 40)) return fail(SWA_ERR_UNSUPPORTED, "%s: tensor too large", name);
+
+    swa::PrefillParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.N = N;
+    p.W = window < N ? window : N;  // W >= N is full causal: identical work and bits
+    p.stride = stride > 0 ? stride : 0;
+    p.c = fabsf(scale) * kLog2e;
+    p.neg = scale < 0.f;
+    p.G = (int)G;
+    p.HG = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+    p.PB = 4 / p.HG;
+    const int BM = swa::kQueriesPerWave * p.PB;
+    p.nqb = (N + BM - 1) / BM;
+    p.ngroups = (int)G / p.HG;
+    const long long total = (long long)B * Hkv * p.ngroups * p.nqb;
+    if (total > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
+    p.total = (int)total;
+    hipError_t e = swa::launch_band_fwd(bf16, d, p.stride > 0, p, stream);
+    if (e != hipSuccess) return fail(SWA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
+    return ok();
+}
+
+int decode(bool bf16, const void* q, const void* kring, const void* vring, const int32_t* pos, void* out, int B,
+           int Hq, int Hkv, int d, float scale, void* workspace, size_t workspace_bytes, int window,
+           hipStream_t stream) {
+    const char* name = bf16 ? "swa_decode" : "swa_decode_f32";
+    if (B < 1 || Hq < 1 || Hkv < 1)
+        return fail(SWA_ERR_INVALID_ARG, "%s: B, Hq, Hkv must be >= 1 (B=%d Hq=%d Hkv=%d)", name, B, Hq, Hkv);
+    if (Hq % Hkv != 0) return fail(SWA_ERR_INVALID_ARG, "%s: Hq (%d) must be a multiple of Hkv (%d)", name, Hq, Hkv);
+    if (window < 1) return fail(SWA_ERR_INVALID_ARG, "%s: window must be >= 1 (got %d)", name, window);
+    if (d != 64 && d != 128) return fail(SWA_ERR_UNSUPPORTED, "%s: head dim %d not built (64 or 128)", name, d);
+    const int G = Hq / Hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(SWA_ERR_UNSUPPORTED, "%s: Hq/Hkv = %d not built (1, 2, 4 or 8)", name, G);
+    if (!aligned16(q) || !aligned16(kring) || !aligned16(vring) || !aligned16(out) || !aligned16(workspace))
+        return fail(SWA_ERR_INVALID_ARG, "%s: q, kring, vring, out, workspace must be non-null and 16-byte aligned",
+                    name);
+    if (pos == nullptr || ((uintptr_t)pos & 3u)) return fail(SWA_ERR_INVALID_ARG, "%s: pos must be non-null, 4-byte aligned", name);
+    if (int rc = check_scale(name, scale)) return rc;
+    const size_t need = swa::decode_workspace_bytes(B, Hq, window, d);
+    if (workspace_bytes < need)
+        return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes is below the %zu needed", name, workspace_bytes,
+                    need);
+    swa::DecodeParams p;
+    p.q = q;
+    p.kring = kring;
+    p.vring = vring;
+    p.pos = pos;
+    p.out = out;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.W = window;
+    p.split_len = swa::kDecodeSplit;
+    p.nsplit = (window + p.split_len - 1) / p.split_len;
+    p.ws_acc = (float*)workspace;
+    p.ws_ml = p.ws_acc + (size_t)B * Hq * p.nsplit * d;
+    p.c = fabsf(scale) * kLog2e;
+    p.neg = scale < 0.f;
+    if ((long long)p.nsplit > 65535 || Hkv > 65535 || B > 65535)
+        return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
+    hipError_t e = swa::launch_decode(bf16, d, G, p, stream);
+    if (e != hipSuccess) return fail(SWA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int swa_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N, int d,
+                 int window, int stride, float scale, hipStream_t stream) {
+    return attn_fwd(true, q, k, v, out, B, Hq, Hkv, N, d, window, stride, scale, stream);
+}
+
+int swa_attn_fwd_f32(const float* q, const float* k, const float* v, float* out, int B, int Hq, int Hkv, int N, int d,
+                     int window, int stride, float scale, hipStream_t stream) {
+    return attn_fwd(false, q, k, v, out, B, Hq, Hkv, N, d, window, stride, scale, stream);
+}
+
+int swa_decode(const void* q, const void* kring, const void* vring, const int32_t* pos, void* out, int B, int Hq,
+               int Hkv, int d, float scale, void* workspace, size_t workspace_bytes, int window, hipStream_t stream) {
+    return decode(true, q, kring, vring, pos, out, B, Hq, Hkv, d, scale, workspace, workspace_bytes, window, stream);
+}
+
+int swa_decode_f32(const float* q, const float* kring, const float* vring, const int32_t* pos, float* out, int B,
+                   int Hq, int Hkv, int d, float scale, void* workspace, size_t workspace_bytes, int window,
+                   hipStream_t stream) {
+    return decode(false, q, kring, vring, pos, out, B, Hq, Hkv, d, scale, workspace, workspace_bytes, window, stream);
+}
+
+size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || window < 1 || (d != 64 && d != 128)) return 0;
+    return swa::decode_workspace_bytes(B, Hq, window, d);
+}
+
+const char* swa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,398 @@
+// Band-tiled causal sliding-window attention forward for CDNA4 (gfx950).
+//
+// What it computes: softmax(scale * Q K^T + M) V row by row, where row i may
+// read key j iff j <= i and (i - j < W or (stride > 0 and j % stride == 0)).
+// The band is the set N_W(i) of the page "SWA：滑动窗口注意力与跨层信息传递"
+// (§3.1, window counting the current position), the strided keys are the
+// "local + strided" mask of the page "注意力变体——滑动窗口、稀疏、差分"
+// (构建它, 第 3 步).  The same pages note that the saving only exists if the
+// out-of-window work is really skipped (SWA page §4.1; the attention-variants
+// page, 稀疏 / 块注意力: never bring the zero entries on chip), so the kernel
+// enumerates only key tiles that meet the band.
+//
+// Structure (one workgroup = 4 waves = 256 threads):
+//  * A workgroup owns 4 blocks of 32 queries: HG query heads that share one
+//    KV head times PB position blocks (HG * PB = 4).  Grouped heads therefore
+//    read every K/V tile from LDS once per workgroup.
+//  * Key tiles of 64 rows are visited from the diagonal tile down to the
+//    lowest tile that meets the band; with stride > 0 a compact list of the
+//    strided keys below the band follows (rows gathered at j = m * stride).
+//    Each tile is copied HBM -> registers -> LDS (16-byte coalesced loads),
+//    double-buffered, one barrier per tile.
+//  * Per wave the score block is computed transposed, S^T = K Q^T, with the
+//    32x32 matrix-core instruction (bf16: 32x32x16, fp32: 32x32x2).  In that
+//    layout a lane owns one query and 32 of the tile's 64 keys; the other 32
+//    sit in lane ^ 32, so the row max needs one cross-lane swap per tile and
+//    the row sum none until the end.  K rows are fed in the order sigma()
+//    below so the lane's probabilities are already the B operand of the
+//    P*V product: O^T += V^T P^T, with V^T fragments read from LDS by the
+//    gfx950 transpose read (bf16) or one dword per lane (fp32).
+//  * Online softmax in the log2 domain; the mask is applied only on tiles
+//    that are not entirely inside every row's band (edge tiles).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+#include <type_traits>
+
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kTileN = kKeysPerTile;  // 64 keys per tile
+constexpr int kQw = kQueriesPerWave;  // 32 queries per wave
+
+// Row of the 32-key block that lane x%32 feeds as the A operand of S^T = K Q^T.
+// The 32x32 result row r of a lane in half g holds element i with
+// r = 8*(i/4) + 4*g + i%4; swapping bits 2 and 3 makes the key behind element
+// i equal to 16*(i/8) + 8*g + i%8, i.e. 8 consecutive keys per half and per
+// 16-key chunk -- exactly the k-slots the P*V instruction expects.
+__device__ __forceinline__ int sigma(int x) {
+    return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// Global work id -> logical id so that consecutive logical ids (consecutive
+// query tiles of one head) land on the same XCD: the dispatcher hands work
+// group x to XCD x % 8, and each XCD has its own L2.
+__device__ __forceinline__ int xcd_remap(int x, int total) {
+    const int per = total >> 3, rem = total & 7;
+    const int xcd = x & 7, idx = x >> 3;
+    return xcd * per + min(xcd, rem) + idx;
+}
+
+// LDS byte offsets of (row, byte-in-row) inside a K or V tile.  16-byte
+// chunks are XOR-swizzled per row so that the matrix-core fragment reads are
+// free of bank conflicts: K rows sigma(0..7) = 0..3, 8..11 must land on 8
+// distinct chunk columns; V transpose reads touch 4 consecutive rows x 32
+// bytes, which must land on 4 distinct chunk pairs.
+template <int RB>
+__device__ __forceinline__ int k_off(int row, int byte) {
+    const int f = (row & 3) | ((row >> 1) & 4);
+    return row * RB + ((((byte >> 4) ^ f)) << 4) + (byte & 15);
+}
+template <int RB>
+__device__ __forceinline__ int v_off(int row, int byte) {
+    const int f = (row & 3) << 1;
+    return row * RB + ((((byte >> 4) ^ f)) << 4) + (byte & 15);
+}
+
+__device__ __forceinline__ float partner_max(float x) {
+    // permlane32_swap(x, x): lanes 0..31 receive (x[l], x[l+32]),
+    // lanes 32..63 receive (x[l-32], x[l]); either way both copies.
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float partner_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(p));
+}
+
+template <bool BF, int D, bool STRIDED>
+__global__ __launch_bounds__(kThreads) void band_fwd_kernel(PrefillParams p) {
+    using elem_t = typename std::conditional<BF, uint16_t, float>::type;
+    using frag_t = typename std::conditional<BF, bf16x8_t, float>::type;
+    constexpr int RB = D * (int)sizeof(elem_t);      // bytes per K/V row
+    constexpr int CPR = RB / 16;                     // 16-byte chunks per row
+    constexpr int TILE_BYTES = kTileN * RB;
+    constexpr int NCH = kTileN * CPR / kThreads;     // chunks per thread per tile
+    constexpr int NDB = D / 32;                      // 32-row blocks of O^T
+    constexpr int KSTEP = BF ? 16 : 2;               // contraction depth per instruction
+    constexpr int NQF = D / KSTEP;
+    static_assert(NCH >= 1 && (kTileN * CPR) % kThreads == 0, "tile copy split");
+
+    __shared__ __attribute__((aligned(16))) char lds[2 * 2 * TILE_BYTES];  // [buffer][K | V]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, l32 = lane & 31;
+
+    // ---- which workgroup tile is this
+    const int L = xcd_remap(blockIdx.x, p.total);
+    const int qb = L % p.nqb;
+    int rest = L / p.nqb;
+    const int hg = rest % p.ngroups;
+    rest /= p.ngroups;
+    const int kvh = rest % p.Hkv;
+    const int b = rest / p.Hkv;
+    const int N = p.N, W = p.W;
+    const int BM = kQw * p.PB;
+    const int q0 = qb * BM;
+    const int h = kvh * p.G + hg * p.HG + (wave % p.HG);
+    const int qw0 = q0 + kQw * (wave / p.HG);
+    const int qi = qw0 + l32;
+
+    const size_t kv_head = (size_t)(b * p.Hkv + kvh) * (size_t)N * D;
+    const size_t q_head = (size_t)(b * p.Hq + h) * (size_t)N * D;
+    const elem_t* kg = (const elem_t*)p.k + kv_head;
+    const elem_t* vg = (const elem_t*)p.v + kv_head;
+    const elem_t* qg = (const elem_t*)p.q + q_head;
+    elem_t* og = (elem_t*)p.out + q_head;
+
+    // ---- key tiles of this workgroup: band tiles kt_hi .. kt_lo, then the
+    // compact strided tiles (keys m*stride < kt_lo*64, read by every row).
+    const int kt_hi = min(N - 1, q0 + BM - 1) / kTileN;
+    const int kt_lo = max(0, q0 - W + 1) / kTileN;
+    const int nband = kt_hi - kt_lo + 1;
+    int M = 0, ncomp = 0;
+    if (STRIDED) {
+        M = (kt_lo * kTileN + p.stride - 1) / p.stride;
+        ncomp = (M + kTileN - 1) / kTileN;
+    }
+    const int ntiles = nband + ncomp;
+
+    // ---- this wave's own band tiles (waves of other position blocks may
+    // need tiles it does not).
+    const bool wave_live = qw0 < N;
+    const int wkt_hi = min(N - 1, qw0 + kQw - 1) / kTileN;
+    const int wkt_lo = max(0, qw0 - W + 1) / kTileN;
+
+    // ---- Q fragments (B operand of S^T = K Q^T), sign folded in
+    frag_t qf[NQF];
+    if constexpr (BF) {
+        const uint32_t flip = p.neg ? 0x80008000u : 0u;
+#pragma unroll
+        for (int c = 0; c < NQF; ++c) {
+            u32x4_t w = {0u, 0u, 0u, 0u};
+            if (qi < N) w = *(const u32x4_t*)(qg + (size_t)qi * D + 16 * c + 8 * g);
+            w ^= flip;
+            qf[c] = __builtin_bit_cast(bf16x8_t, w);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < NQF; ++c) {
+            float x = (qi < N) ? qg[(size_t)qi * D + 2 * c + g] : 0.f;
+            qf[c] = p.neg ? -x : x;
+        }
+    }
+
+    // ---- tile copy HBM -> registers -> LDS
+    u32x4_t kr[NCH], vr[NCH];
+    auto load_tile = [&](int t) {
+#pragma unroll
+        for (int it = 0; it < NCH; ++it) {
+            const int u = tid + kThreads * it;
+            const int row = u / CPR, ch = u % CPR;
+            int key;
+            bool ok;
+            if (t < nband) {
+                key = (kt_hi - t) * kTileN + row;
+                ok = key < N;
+            } else {
+                const int m = (t - nband) * kTileN + row;
+                ok = m < M;
+                key = m * p.stride;
+            }
+            u32x4_t kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+            if (ok) {
+                kk = *(const u32x4_t*)((const char*)(kg + (size_t)key * D) + ch * 16);
+                vv = *(const u32x4_t*)((const char*)(vg + (size_t)key * D) + ch * 16);
+            }
+            kr[it] = kk;
+            vr[it] = vv;
+        }
+    };
+    auto store_tile = [&](int buf) {
+        char* kl = lds + buf * 2 * TILE_BYTES;
+        char* vl = kl + TILE_BYTES;
+#pragma unroll
+        for (int it = 0; it < NCH; ++it) {
+            const int u = tid + kThreads * it;
+            const int row = u / CPR, ch = u % CPR;
+            *(u32x4_t*)(kl + k_off<RB>(row, ch * 16)) = kr[it];
+            *(u32x4_t*)(vl + v_off<RB>(row, ch * 16)) = vr[it];
+        }
+    };
+
+    f32x16_t oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    const float c = p.c;
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < ntiles) load_tile(t + 1);
+
+        const bool band = t < nband;
+        const int kt = kt_hi - t;
+        const bool active = wave_live && (band ? (kt <= wkt_hi && (STRIDED || kt >= wkt_lo)) : true);
+        if (active) {
+            const char* kl = lds + buf * 2 * TILE_BYTES;
+            const char* vl = kl + TILE_BYTES;
+
+            // S^T for the two 32-key halves of the tile
+            f32x16_t s[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+                const int krow = kb * 32 + sigma(l32);
+#pragma unroll
+                for (int cc = 0; cc < NQF; ++cc) {
+                    if constexpr (BF) {
+                        const bf16x8_t a = *(const bf16x8_t*)(kl + k_off<RB>(krow, (16 * cc + 8 * g) * 2));
+                        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], s[kb], 0, 0, 0);
+                    } else {
+                        const float a = *(const float*)(kl + k_off<RB>(krow, (2 * cc + g) * 4));
+                        s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[cc], s[kb], 0, 0, 0);
+                    }
+                }
+            }
+
+            // mask: only tiles not entirely inside every row's band
+            const int j0 = kt * kTileN;
+            const bool edge = band ? !(j0 + kTileN - 1 <= qw0 && j0 >= qw0 + kQw - W)
+                                   : ((t - nband + 1) * kTileN > M);
+            if (edge) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int r = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
+                        bool ok;
+                        if (band) {
+                            const int j = j0 + r;
+                            const int dist = qi - j;
+                            ok = dist >= 0 && (dist < W || (STRIDED && (j % p.stride) == 0));
+                        } else {
+                            ok = (t - nband) * kTileN + r < M;
+                        }
+                        if (!ok) s[kb][i] = -INFINITY;
+                    }
+            }
+
+            // online softmax (log2 domain); the lane pair (l, l^32) shares a query
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+            mx = partner_max(mx);
+            const float m_new = fmaxf(m_run, mx * c);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            m_run = m_new;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -m_use));
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+
+            // O^T += V^T P^T.  The row sum adds the same probabilities the
+            // product uses: bf16-rounded ones (packed dot with (1, 1)), so
+            // the output is an exact convex combination of V rows.
+            float rs = 0.f;
+            if constexpr (BF) {
+                const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+                for (int c2 = 0; c2 < 4; ++c2) {
+                    // pairs are built as bf16x2 values and only whole vectors are
+                    // bit-cast: extracting a dword of a bf16x8 and bit-casting it
+                    // to bf16x2 mis-compiles (every pair reads element 0).
+                    u32x4_t pw;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bf16x2_t pr = {(__bf16)s[c2 >> 1][8 * (c2 & 1) + 2 * e],
+                                             (__bf16)s[c2 >> 1][8 * (c2 & 1) + 2 * e + 1]};
+                        rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+                        pw[e] = __builtin_bit_cast(uint32_t, pr);
+                    }
+                    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+                    const int row0 = 16 * c2 + 8 * g + ((lane & 15) >> 2);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const int byte = (db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+                        const i16x4_t lo = lds_read_tr16(vl + v_off<RB>(row0, byte));
+                        const i16x4_t hi = lds_read_tr16(vl + v_off<RB>(row0 + 4, byte));
+                        const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
+                        const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
+                        const u32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
+                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8_t, a4), pb, oacc[db], 0, 0, 0);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        rs += s[kb][i];
+                        const int r = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db) {
+                            const float a = *(const float*)(vl + v_off<RB>(r, (db * 32 + l32) * 4));
+                            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][i], oacc[db], 0, 0, 0);
+                        }
+                    }
+            }
+            l_run = l_run * alpha + rs;
+        }
+
+        if (t + 1 < ntiles) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O / l, lane holds d = 32*db + 8*quad + 4*g + 0..3
+    const float lt = partner_sum(l_run);
+    if (!wave_live || qi >= N) return;
+    const float inv = 1.f / lt;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int quad = 0; quad < 4; ++quad) {
+            const int d0 = db * 32 + 8 * quad + 4 * g;
+            const float o0 = oacc[db][4 * quad + 0] * inv, o1 = oacc[db][4 * quad + 1] * inv;
+            const float o2 = oacc[db][4 * quad + 2] * inv, o3 = oacc[db][4 * quad + 3] * inv;
+            if constexpr (BF) {
+                typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                const bf16x4_t o = {(__bf16)o0, (__bf16)o1, (__bf16)o2, (__bf16)o3};
+                *(bf16x4_t*)(og + (size_t)qi * D + d0) = o;
+            } else {
+                typedef float f32x4_t __attribute__((ext_vector_type(4)));
+                const f32x4_t o = {o0, o1, o2, o3};
+                *(f32x4_t*)(og + (size_t)qi * D + d0) = o;
+            }
+        }
+}
+
+template <bool BF, int D, bool STRIDED>
+hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
+    hipLaunchKernelGGL((band_fwd_kernel<BF, D, STRIDED>), dim3(p.total), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_band_fwd(bool bf16, int d, bool strided, const PrefillParams& p, hipStream_t s) {
+    if (bf16) {
+        if (d == 128) return strided ? launch_one<true, 128, true>(p, s) : launch_one<true, 128, false>(p, s);
+        return strided ? launch_one<true, 64, true>(p, s) : launch_one<true, 64, false>(p, s);
+    }
+    if (d == 128) return strided ? launch_one<false, 128, true>(p, s) : launch_one<false, 128, false>(p, s);
+    return strided ? launch_one<false, 64, true>(p, s) : launch_one<false, 64, false>(p, s);
+}
+
+}  // namespace swa

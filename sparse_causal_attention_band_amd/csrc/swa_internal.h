@@ -1,0 +1,59 @@
+// Internal declarations shared by the kernel translation units and the C ABI
+// layer.  Not installed; the public interface is include/swa_attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swa {
+
+// ---------------------------------------------------------------- prefill
+struct PrefillParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    int B, Hq, Hkv, N;
+    int W;        // window, already clamped to N
+    int stride;   // > 0 only for the strided instantiation
+    float c;      // |scale| * log2(e): scores are kept in the log2 domain
+    int neg;      // scale < 0: queries enter with flipped sign (exact)
+    int G;        // Hq / Hkv
+    int HG;       // query heads of one KV head that share a workgroup
+    int PB;       // 32-query blocks per head in a workgroup (HG * PB == 4)
+    int nqb;      // query tiles per head
+    int ngroups;  // G / HG
+    int total;    // workgroups in the grid
+};
+
+// Launch the band kernel for one (dtype, head dim, strided) combination.
+hipError_t launch_band_fwd(bool bf16, int d, bool strided, const PrefillParams& p, hipStream_t s);
+
+// Rows of one workgroup tile, for host-side bookkeeping and tests.
+constexpr int kQueriesPerWave = 32;
+constexpr int kKeysPerTile = 64;
+
+// ---------------------------------------------------------------- decode
+struct DecodeParams {
+    const void* q;
+    const void* kring;
+    const void* vring;
+    const int32_t* pos;
+    void* out;
+    float* ws_acc;   // [B, Hq, nsplit, d]  un-normalised weighted V sums
+    float* ws_ml;    // [B, Hq, nsplit, 2]  (running max in log2 units, sum)
+    int B, Hq, Hkv, W;
+    int nsplit;      // ceil(W / split_len)
+    int split_len;   // ring slots per split (multiple of the 64-slot tile)
+    float c;         // |scale| * log2(e)
+    int neg;
+};
+
+constexpr int kDecodeSplit = 512;
+
+hipError_t launch_decode(bool bf16, int d, int G, const DecodeParams& p, hipStream_t s);
+
+size_t decode_workspace_bytes(int B, int Hq, int W, int d);
+
+}  // namespace swa

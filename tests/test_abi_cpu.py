@@ -1,0 +1,115 @@
+"""Host-side checks that need no GPU: the built library loads, exports every
+symbol the public header declares, and rejects bad arguments with the
+documented codes before it launches anything."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import sparse_causal_attention_band_amd as swa
+from sparse_causal_attention_band_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swa_attn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"SWA_API\s+[\w\s\*]+?\b(swa_\w+)\s*\(", text)
+
+
+def test_header_declares_the_abi():
+    names = _declared()
+    assert sorted(names) == sorted(swa.SIGNATURES), names
+
+
+def test_library_exports_every_declared_symbol():
+    L = swa.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_only_the_abi_is_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", swa.LIB_PATH], capture_output=True, text=True).stdout
+    text_syms = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert text_syms == sorted(_declared())
+
+
+A = 1 << 12  # a fake, 16-byte aligned "device" address: never dereferenced
+
+
+def _fwd(**kw):
+    args = dict(q=A, k=A * 2, v=A * 3, out=A * 1024, B=1, Hq=4, Hkv=2, N=16, d=64, window=4, stride=0,
+                scale=0.125, stream=None)
+    args.update(kw)
+    fn = swa.lib().swa_attn_fwd
+    return fn(args["q"], args["k"], args["v"], args["out"], args["B"], args["Hq"], args["Hkv"], args["N"],
+              args["d"], args["window"], args["stride"], args["scale"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -1), (dict(N=0), -1), (dict(Hq=0), -1), (dict(Hkv=0), -1), (dict(Hq=3, Hkv=2), -1),
+    (dict(window=0), -1), (dict(window=-7), -1), (dict(d=32), -2), (dict(d=96), -2),
+    (dict(q=None), -1), (dict(k=A + 8), -1), (dict(out=A + 2), -1), (dict(scale=0.0), -1),
+    (dict(scale=float("inf")), -1), (dict(scale=float("nan")), -1), (dict(out=A), -1),
+])
+def test_fwd_rejects_bad_arguments(kw, code):
+    rc = _fwd(**kw)
+    assert rc == code
+    assert swa.lib().swa_last_error().decode().startswith("swa_attn_fwd")
+
+
+def _dec(**kw):
+    ws = swa.lib().swa_decode_workspace_bytes(2, 8, 2, 128, 64)
+    args = dict(q=A, kr=A * 2, vr=A * 3, pos=A * 4, out=A * 5, B=2, Hq=8, Hkv=2, d=128, scale=0.1,
+                ws=A * 6, wsb=ws, window=64, stream=None)
+    args.update(kw)
+    return swa.lib().swa_decode(args["q"], args["kr"], args["vr"], args["pos"], args["out"], args["B"],
+                                args["Hq"], args["Hkv"], args["d"], args["scale"], args["ws"], args["wsb"],
+                                args["window"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -1), (dict(Hq=6, Hkv=4), -1), (dict(window=0), -1), (dict(d=80), -2),
+    (dict(Hq=6, Hkv=2), -2), (dict(Hq=32, Hkv=2), -2), (dict(pos=None), -1), (dict(pos=A + 2), -1),
+    (dict(ws=None), -1), (dict(wsb=16), -1), (dict(kr=A + 4), -1), (dict(scale=0.0), -1),
+])
+def test_decode_rejects_bad_arguments(kw, code):
+    assert _dec(**kw) == code
+    assert swa.lib().swa_last_error().decode().startswith("swa_decode")
+
+
+def test_workspace_size_formula():
+    L = swa.lib()
+    # splits of 512 slots; per (sequence, query head, split): d floats + (max, sum)
+    assert L.swa_decode_workspace_bytes(64, 32, 8, 128, 4096) == 64 * 32 * 8 * (128 + 2) * 4
+    assert L.swa_decode_workspace_bytes(1, 1, 1, 64, 1) == 1 * 1 * 1 * 66 * 4
+    assert L.swa_decode_workspace_bytes(1, 1, 1, 64, 513) == 2 * 66 * 4
+    assert L.swa_decode_workspace_bytes(1, 3, 2, 64, 8) == 0
+    assert L.swa_decode_workspace_bytes(1, 2, 1, 100, 8) == 0
+
+
+def test_python_wrapper_refuses_host_tensors():
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        swa.attn_fwd(q, q, q, window=4)
+    with pytest.raises(TypeError):
+        swa.attn_fwd(q.half(), q.half(), q.half(), window=4)
+
+
+def test_inputs_are_seeded_and_shaped():
+    a = inputs.prefill_inputs(inputs.STRIDED, N=100)
+    b = inputs.prefill_inputs(inputs.STRIDED, N=100)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y) and x.dtype == torch.bfloat16
+    assert a[0].shape == (1, 16, 100, 64)
+    q, kr, vr, pos = inputs.decode_inputs(inputs.DECODE, B=8)
+    assert q.shape == (8, 32, 128) and kr.shape == (8, 8, 4096, 128) and pos.dtype == torch.int32
+    assert int(pos.min()) >= 1 and int(pos.max()) <= 131072
+    m = inputs.prefill_inputs(inputs.MISTRAL, N=64)
+    # Q and K carry the 0.5 factor, V does not
+    assert float(m[0].float().std()) < 0.7 and float(m[2].float().std()) > 0.8
