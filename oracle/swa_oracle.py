@@ -207,44 +207,42 @@ def attn_fwd(q, k, v, window: int, stride: int = 0, scale: Optional[float] = Non
     return out
 
 
-def _pool_job(args):
-    q, k, v, rows, window, stride, scale = args
-    return _head_rows(q, k, v, rows, window, stride, scale)
+_POOL_INPUT = None
+
+
+def _pool_job(bh):
+    from threadpoolctl import threadpool_limits
+
+    q, k, v, rows, window, stride, scale, G = _POOL_INPUT
+    b, h = bh
+    with threadpool_limits(limits=1):
+        return _head_rows(q[b, h], k[b, h // G], v[b, h // G], rows, window, stride, scale)
 
 
 def attn_fwd_parallel(q, k, v, window: int, stride: int, scale: float,
                       rows: np.ndarray, workers: Optional[int] = None):
     """Same arithmetic as ``attn_fwd`` for the given query rows of every
-    (b, h), spread over a process pool (one (b, h) per task, one BLAS thread
-    per worker).  Returns (float64 [B, Hq, len(rows), d], workers used)."""
+    (b, h), spread over a forked process pool (one (b, h) per task, one BLAS
+    thread per worker; the workers inherit the inputs instead of receiving
+    copies).  Returns (float64 [B, Hq, len(rows), d], workers used)."""
     import multiprocessing as mp
 
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
+    global _POOL_INPUT
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
     _check(q, k, v, window)
     B, Hq, N, d = q.shape
     G = Hq // k.shape[1]
     if workers is None:
         workers = len(os.sched_getaffinity(0))
     rows = np.asarray(rows, dtype=np.int64)
-    jobs = [(q[b, h], k[b, h // G], v[b, h // G], rows, window, stride, scale)
-            for b in range(B) for h in range(Hq)]
-    env_keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
-    saved = {kk: os.environ.get(kk) for kk in env_keys}
-    for kk in env_keys:
-        os.environ[kk] = "1"
+    _POOL_INPUT = (q, k, v, rows, window, stride, scale, G)
     try:
         ctx = mp.get_context("fork")
         with ctx.Pool(workers) as pool:
-            parts = pool.map(_pool_job, jobs, chunksize=1)
+            parts = pool.map(_pool_job, [(b, h) for b in range(B) for h in range(Hq)], chunksize=1)
     finally:
-        for kk, val in saved.items():
-            if val is None:
-                os.environ.pop(kk, None)
-            else:
-                os.environ[kk] = val
-    out = np.stack(parts).reshape(B, Hq, len(rows), d)
+        _POOL_INPUT = None
+    out = np.stack(parts).reshape(B, Hq, len(rows), v.shape[3])
     return out, workers
 
 
