@@ -17,8 +17,8 @@
 //  * Key tiles of 64 rows are visited from the diagonal tile down to the
 //    lowest tile that meets the band; with stride > 0 a compact list of the
 //    strided keys below the band follows (rows gathered at j = m * stride).
-//    Each tile is copied HBM -> registers -> LDS (16-byte coalesced loads),
-//    double-buffered, one barrier per tile.
+//    Each tile is copied HBM -> LDS directly (global_load_lds, 16 bytes per
+//    lane, coalesced), double-buffered, one barrier per tile.
 //  * Per wave the score block is computed transposed, S^T = K Q^T, with the
 //    32x32 matrix-core instruction (bf16: 32x32x16, fp32: 32x32x2).  In that
 //    layout a lane owns one query and 32 of the tile's 64 keys; the other 32
@@ -102,7 +102,7 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
 }
 
 template <bool BF, int D, bool STRIDED>
-__global__ __launch_bounds__(kThreads) void band_fwd_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) {
     using elem_t = typename std::conditional<BF, uint16_t, float>::type;
     using frag_t = typename std::conditional<BF, bf16x8_t, float>::type;
     constexpr int RB = D * (int)sizeof(elem_t);      // bytes per K/V row
@@ -179,41 +179,32 @@ __global__ __launch_bounds__(kThreads) void band_fwd_kernel(PrefillParams p) {
         }
     }
 
-    // ---- tile copy HBM -> registers -> LDS
-    u32x4_t kr[NCH], vr[NCH];
-    auto load_tile = [&](int t) {
-#pragma unroll
-        for (int it = 0; it < NCH; ++it) {
-            const int u = tid + kThreads * it;
-            const int row = u / CPR, ch = u % CPR;
-            int key;
-            bool ok;
-            if (t < nband) {
-                key = (kt_hi - t) * kTileN + row;
-                ok = key < N;
-            } else {
-                const int m = (t - nband) * kTileN + row;
-                ok = m < M;
-                key = m * p.stride;
-            }
-            u32x4_t kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-            if (ok) {
-                kk = *(const u32x4_t*)((const char*)(kg + (size_t)key * D) + ch * 16);
-                vv = *(const u32x4_t*)((const char*)(vg + (size_t)key * D) + ch * 16);
-            }
-            kr[it] = kk;
-            vr[it] = vv;
-        }
-    };
-    auto store_tile = [&](int buf) {
+    // ---- tile copy HBM -> LDS without registers: each wave's
+    // global_load_lds_dwordx4 fills one contiguous 1 KiB block of LDS (lane i
+    // writes bytes 16i..16i+15 of it), so the swizzle is applied by choosing
+    // which global 16-byte chunk each lane fetches (the XOR is its own
+    // inverse).  Rows past the end are clamped to a valid row: those keys are
+    // always masked, and the copy never leaves non-finite bits in LDS.
+    auto issue_tile = [&](int t, int buf) {
         char* kl = lds + buf * 2 * TILE_BYTES;
         char* vl = kl + TILE_BYTES;
 #pragma unroll
         for (int it = 0; it < NCH; ++it) {
-            const int u = tid + kThreads * it;
-            const int row = u / CPR, ch = u % CPR;
-            *(u32x4_t*)(kl + k_off<RB>(row, ch * 16)) = kr[it];
-            *(u32x4_t*)(vl + v_off<RB>(row, ch * 16)) = vr[it];
+            const int blk = (wave * NCH + it) * 1024;  // wave-uniform LDS block
+            const int P = blk + lane * 16;
+            const int row = P / RB, chp = (P % RB) >> 4;
+            int key;
+            if (t < nband) {
+                key = min((kt_hi - t) * kTileN + row, N - 1);
+            } else {
+                key = min((t - nband) * kTileN + row, M - 1) * p.stride;
+            }
+            const int fk = (row & 3) | ((row >> 1) & 4);
+            const int fv = (row & 3) << 1;
+            const char* ksrc = (const char*)(kg + (size_t)key * D) + ((chp ^ fk) << 4);
+            const char* vsrc = (const char*)(vg + (size_t)key * D) + ((chp ^ fv) << 4);
+            __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)(kl + blk), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)(vl + blk), 16, 0, 0);
         }
     };
 
@@ -225,13 +216,15 @@ __global__ __launch_bounds__(kThreads) void band_fwd_kernel(PrefillParams p) {
     float m_run = -INFINITY, l_run = 0.f;
     const float c = p.c;
 
-    load_tile(0);
-    store_tile(0);
+    issue_tile(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
-        if (t + 1 < ntiles) load_tile(t + 1);
+        // the other buffer was last read in iteration t-1, which every wave
+        // finished before the barrier that closed it
+        if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
 
         const bool band = t < nband;
         const int kt = kt_hi - t;
@@ -264,6 +257,12 @@ __global__ __launch_bounds__(kThreads) void band_fwd_kernel(PrefillParams p) {
             const bool edge = band ? !(j0 + kTileN - 1 <= qw0 && j0 >= qw0 + kQw - W)
                                    : ((t - nband + 1) * kTileN > M);
             if (edge) {
+                // bit o of smask: key j0 + o is a multiple of the stride
+                uint64_t smask = 0;
+                if (STRIDED && band) {
+                    const int r0 = j0 % p.stride;
+                    for (int o = r0 == 0 ? 0 : p.stride - r0; o < kTileN; o += p.stride) smask |= 1ull << o;
+                }
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -273,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void band_fwd_kernel(PrefillParams p) {
                         if (band) {
                             const int j = j0 + r;
                             const int dist = qi - j;
-                            ok = dist >= 0 && (dist < W || (STRIDED && (j % p.stride) == 0));
+                            ok = dist >= 0 && (dist < W || (STRIDED && ((smask >> r) & 1)));
                         } else {
                             ok = (t - nband) * kTileN + r < M;
                         }
@@ -288,18 +287,29 @@ __global__ __launch_bounds__(kThreads) void band_fwd_kernel(PrefillParams p) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
             mx = partner_max(mx);
-            const float m_new = fmaxf(m_run, mx * c);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            m_run = m_new;
+            // The reference max moves only when the tile max exceeds it by
+            // more than 8 (log2 units): probabilities then stay below 2^8,
+            // which the fp32 sums and the bf16 P operand carry without loss,
+            // and most tiles skip the O / l rescale.  Lanes l and l^32 see the
+            // same max, so they always take the same decision.
+            const float m_cand = fmaxf(m_run, mx * c);
+            const bool grow = m_cand > m_run + 8.f;  // false while both are -inf
+            float alpha = 1.f;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                if (grow) {
+                    alpha = __builtin_amdgcn_exp2f(m_run - m_cand);  // 0 on the first finite max
+                    m_run = m_cand;
+                }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+            }
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // row with no allowed key yet
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -m_use));
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
 
             // O^T += V^T P^T.  The row sum adds the same probabilities the
             // product uses: bf16-rounded ones (packed dot with (1, 1)), so
@@ -351,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void band_fwd_kernel(PrefillParams p) {
             l_run = l_run * alpha + rs;
         }
 
-        if (t + 1 < ntiles) store_tile(buf ^ 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 
