@@ -69,21 +69,19 @@ __device__ __forceinline__ int xcd_remap(int x, int total) {
     return xcd * per + min(xcd, rem) + idx;
 }
 
-// LDS byte offsets of (row, byte-in-row) inside a K or V tile.  16-byte
-// chunks are XOR-swizzled per row so that the matrix-core fragment reads are
-// free of bank conflicts: K rows sigma(0..7) = 0..3, 8..11 must land on 8
-// distinct chunk columns; V transpose reads touch 4 consecutive rows x 32
-// bytes, which must land on 4 distinct chunk pairs.
-template <int RB>
-__device__ __forceinline__ int k_off(int row, int byte) {
-    const int f = (row & 3) | ((row >> 1) & 4);
-    return row * RB + ((((byte >> 4) ^ f)) << 4) + (byte & 15);
-}
-template <int RB>
-__device__ __forceinline__ int v_off(int row, int byte) {
-    const int f = (row & 3) << 1;
-    return row * RB + ((((byte >> 4) ^ f)) << 4) + (byte & 15);
-}
+// LDS tile layouts.  gfx950's LDS serves 256 bytes (64 banks) per cycle:
+// 16 lanes of a 16-byte read, 32 lanes of an 8-byte read.
+//  * K: rows in groups of 16, 16-byte chunks column-major inside a group:
+//    position p, chunk c at ((p >> 4) * CPR + c) * 256 + (p & 15) * 16.
+//    The 16 lanes served together read 16 consecutive positions of one chunk
+//    column, 256 contiguous bytes.  Rows are stored in sigma order (position
+//    p holds key row sigma(p)), so the lanes needing rows sigma(0..15) read
+//    positions 0..15.  One 1 KiB copy block is 16 rows x 64 bytes of HBM.
+//  * V: row-major with a 64-byte pad after each row (stride RB + 64).  An
+//    8-byte transpose read by 32 lanes touches 4 consecutive rows x 64 bytes,
+//    which the pad spreads over the 4 quarters of the banks.  Copy lanes that
+//    fall on the pad are switched off.
+// Every fragment address is then (per-lane base) + (compile-time offset).
 
 __device__ __forceinline__ float partner_max(float x) {
     // permlane32_swap(x, x): lanes 0..31 receive (x[l], x[l+32]),
@@ -107,14 +105,25 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     using frag_t = typename std::conditional<BF, bf16x8_t, float>::type;
     constexpr int RB = D * (int)sizeof(elem_t);      // bytes per K/V row
     constexpr int CPR = RB / 16;                     // 16-byte chunks per row
-    constexpr int TILE_BYTES = kTileN * RB;
+    constexpr int TILE_BYTES = kTileN * RB;          // K tile
+    constexpr int RBV = RB + 64;                     // padded V row
+    constexpr int VTILE_BYTES = kTileN * RBV;        // V tile
+    constexpr int NCHV = VTILE_BYTES / (kThreads * 16);  // V copy blocks per wave
     constexpr int NCH = kTileN * CPR / kThreads;     // chunks per thread per tile
     constexpr int NDB = D / 32;                      // 32-row blocks of O^T
     constexpr int KSTEP = BF ? 16 : 2;               // contraction depth per instruction
     constexpr int NQF = D / KSTEP;
     static_assert(NCH >= 1 && (kTileN * CPR) % kThreads == 0, "tile copy split");
+    static_assert(VTILE_BYTES % (kThreads * 16) == 0, "V tile copy split");
 
-    __shared__ __attribute__((aligned(16))) char lds[2 * 2 * TILE_BYTES];  // [buffer][K | V]
+    // Two K/V buffers as four distinct LDS objects: every access below names
+    // its buffer statically (the tile loop is unrolled by two), so the
+    // compiler can tell the in-flight copy of tile t+1 from the reads of tile
+    // t and does not drain the copy before reading.
+    __shared__ __attribute__((aligned(16))) char kb0[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char vb0[VTILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char kb1[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char vb1[VTILE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -179,32 +188,45 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
         }
     }
 
+    // ---- per-lane LDS bases of the fragment reads
+    // K: position l32 (+32 per key half), chunk 2*cc + g (bf16) or cc/2 (fp32)
+    const int k_lane = BF ? ((((l32 >> 4) * CPR + g) << 8) + ((l32 & 15) << 4))
+                          : ((((l32 >> 4) * CPR) << 8) + ((l32 & 15) << 4) + (g << 2));
+    // V (bf16 transpose read): row 8*g + (lane&15)/4 (+16*c2 + 4*rd),
+    // element 16*((lane>>4)&1) + 4*(lane&3) (+32*db).  fp32: row 8*g, element l32.
+    const int v_lane = BF ? ((8 * g + ((lane & 15) >> 2)) * RBV + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2)
+                          : (8 * g * RBV + l32 * 4);
+
     // ---- tile copy HBM -> LDS without registers: each wave's
     // global_load_lds_dwordx4 fills one contiguous 1 KiB block of LDS (lane i
-    // writes bytes 16i..16i+15 of it), so the swizzle is applied by choosing
-    // which global 16-byte chunk each lane fetches (the XOR is its own
-    // inverse).  Rows past the end are clamped to a valid row: those keys are
+    // writes bytes 16i..16i+15 of it), so the layout is applied by choosing
+    // which global 16-byte chunk each lane fetches.  Rows past the end are clamped to a valid row: those keys are
     // always masked, and the copy never leaves non-finite bits in LDS.
-    auto issue_tile = [&](int t, int buf) {
-        char* kl = lds + buf * 2 * TILE_BYTES;
-        char* vl = kl + TILE_BYTES;
+    auto issue_tile = [&](int t, char* kl, char* vl) __attribute__((always_inline)) {
+        // key row behind tile row r
+        auto key_of = [&](int r) __attribute__((always_inline)) {
+            return t < nband ? min((kt_hi - t) * kTileN + r, N - 1)
+                             : min((t - nband) * kTileN + r, M - 1) * p.stride;
+        };
 #pragma unroll
         for (int it = 0; it < NCH; ++it) {
             const int blk = (wave * NCH + it) * 1024;  // wave-uniform LDS block
             const int P = blk + lane * 16;
-            const int row = P / RB, chp = (P % RB) >> 4;
-            int key;
-            if (t < nband) {
-                key = min((kt_hi - t) * kTileN + row, N - 1);
-            } else {
-                key = min((t - nband) * kTileN + row, M - 1) * p.stride;
+            const int within = P % (CPR * 256);
+            const int pos = (P / (CPR * 256)) * 16 + ((within >> 4) & 15);
+            const int ch = within >> 8;
+            const char* src = (const char*)(kg + (size_t)key_of(sigma(pos)) * D) + (ch << 4);
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(kl + blk), 16, 0, 0);
+        }
+#pragma unroll
+        for (int it = 0; it < NCHV; ++it) {
+            const int blk = (wave * NCHV + it) * 1024;
+            const int P = blk + lane * 16;
+            const int row = P / RBV, inrow = P % RBV;
+            if (inrow < RB) {
+                const char* src = (const char*)(vg + (size_t)key_of(row) * D) + inrow;
+                __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(vl + blk), 16, 0, 0);
             }
-            const int fk = (row & 3) | ((row >> 1) & 4);
-            const int fv = (row & 3) << 1;
-            const char* ksrc = (const char*)(kg + (size_t)key * D) + ((chp ^ fk) << 4);
-            const char* vsrc = (const char*)(vg + (size_t)key * D) + ((chp ^ fv) << 4);
-            __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)(kl + blk), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)(vl + blk), 16, 0, 0);
         }
     };
 
@@ -216,37 +238,27 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     float m_run = -INFINITY, l_run = 0.f;
     const float c = p.c;
 
-    issue_tile(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        // the other buffer was last read in iteration t-1, which every wave
-        // finished before the barrier that closed it
-        if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
-
+    auto compute_tile = [&](int t, const char* kl, const char* vl) __attribute__((always_inline)) {
         const bool band = t < nband;
         const int kt = kt_hi - t;
         const bool active = wave_live && (band ? (kt <= wkt_hi && (STRIDED || kt >= wkt_lo)) : true);
         if (active) {
-            const char* kl = lds + buf * 2 * TILE_BYTES;
-            const char* vl = kl + TILE_BYTES;
 
-            // S^T for the two 32-key halves of the tile
+            // S^T for the two 32-key halves of the tile; the lane feeds key
+            // row kb*32 + sigma(l32), stored at position kb*32 + l32
             f32x16_t s[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-                const int krow = kb * 32 + sigma(l32);
 #pragma unroll
                 for (int cc = 0; cc < NQF; ++cc) {
                     if constexpr (BF) {
-                        const bf16x8_t a = *(const bf16x8_t*)(kl + k_off<RB>(krow, (16 * cc + 8 * g) * 2));
+                        const bf16x8_t a = *(const bf16x8_t*)(kl + k_lane + ((kb * 2 * CPR + 2 * cc) << 8));
                         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], s[kb], 0, 0, 0);
                     } else {
-                        const float a = *(const float*)(kl + k_off<RB>(krow, (2 * cc + g) * 4));
+                        const float a =
+                            *(const float*)(kl + k_lane + ((kb * 2 * CPR + (cc >> 1)) << 8) + ((cc & 1) << 3));
                         s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[cc], s[kb], 0, 0, 0);
                     }
                 }
@@ -331,12 +343,13 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
                         pw[e] = __builtin_bit_cast(uint32_t, pr);
                     }
                     const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
-                    const int row0 = 16 * c2 + 8 * g + ((lane & 15) >> 2);
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) {
-                        const int byte = (db * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-                        const i16x4_t lo = lds_read_tr16(vl + v_off<RB>(row0, byte));
-                        const i16x4_t hi = lds_read_tr16(vl + v_off<RB>(row0 + 4, byte));
+                        // rows 16*c2 + 8*g + 4*rd + (lane&15)/4, 4 elements at
+                        // d = 32*db + 16*((lane>>4)&1) + 4*(lane&3)
+                        const char* vp = vl + v_lane + 16 * c2 * RBV + 64 * db;
+                        const i16x4_t lo = lds_read_tr16(vp);
+                        const i16x4_t hi = lds_read_tr16(vp + 4 * RBV);
                         const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
                         const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
                         const u32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
@@ -350,19 +363,35 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         rs += s[kb][i];
-                        const int r = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
 #pragma unroll
                         for (int db = 0; db < NDB; ++db) {
-                            const float a = *(const float*)(vl + v_off<RB>(r, (db * 32 + l32) * 4));
+                            // row kb*32 + 16*(i>>3) + 8*g + (i&7), d = 32*db + l32
+                            const float a = *(const float*)(vl + v_lane +
+                                                            (kb * 32 + 16 * (i >> 3) + (i & 7)) * RBV + 128 * db);
                             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][i], oacc[db], 0, 0, 0);
                         }
                     }
             }
             l_run = l_run * alpha + rs;
         }
+    };
 
+    // A buffer is refilled only after the barrier that closes the iteration
+    // which last read it.
+    issue_tile(0, kb0, vb0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+        if (t + 1 < ntiles) issue_tile(t + 1, kb1, vb1);
+        compute_tile(t, kb0, vb0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        if (t + 1 < ntiles) {
+            if (t + 2 < ntiles) issue_tile(t + 2, kb0, vb0);
+            compute_tile(t + 1, kb1, vb1);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: O / l, lane holds d = 32*db + 8*quad + 4*g + 0..3
