@@ -163,28 +163,27 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     }
     const int ntiles = nband + ncomp;
 
-    // ---- this wave's own band tiles (waves of other position blocks may
-    // need tiles it does not).
-    const bool wave_live = qw0 < N;
-    const int wkt_hi = min(N - 1, qw0 + kQw - 1) / kTileN;
-    const int wkt_lo = max(0, qw0 - W + 1) / kTileN;
+    const bool wave_live = qw0 < N;  // some row of this wave is a real query
 
     // ---- Q fragments (B operand of S^T = K Q^T), sign folded in
     frag_t qf[NQF];
     if constexpr (BF) {
         const uint32_t flip = p.neg ? 0x80008000u : 0u;
+        // rows past N read row N-1 and are zeroed (never stored)
+        const uint32_t keep = qi < N ? 0xffffffffu : 0u;
+        const size_t qrow = (size_t)min(qi, N - 1) * D;
 #pragma unroll
         for (int c = 0; c < NQF; ++c) {
-            u32x4_t w = {0u, 0u, 0u, 0u};
-            if (qi < N) w = *(const u32x4_t*)(qg + (size_t)qi * D + 16 * c + 8 * g);
-            w ^= flip;
+            u32x4_t w = *(const u32x4_t*)(qg + qrow + 16 * c + 8 * g);
+            w = (w & keep) ^ flip;
             qf[c] = __builtin_bit_cast(bf16x8_t, w);
         }
     } else {
+        const size_t qrow = (size_t)min(qi, N - 1) * D;
 #pragma unroll
         for (int c = 0; c < NQF; ++c) {
-            float x = (qi < N) ? qg[(size_t)qi * D + 2 * c + g] : 0.f;
-            qf[c] = p.neg ? -x : x;
+            const float x = qg[qrow + 2 * c + g];
+            qf[c] = qi < N ? (p.neg ? -x : x) : 0.f;
         }
     }
 
@@ -202,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     // writes bytes 16i..16i+15 of it), so the layout is applied by choosing
     // which global 16-byte chunk each lane fetches.  Rows past the end are clamped to a valid row: those keys are
     // always masked, and the copy never leaves non-finite bits in LDS.
-    auto issue_tile = [&](int t, char* kl, char* vl) __attribute__((always_inline)) {
+    auto issue_tile = [&](int t, char* kl, char* vl, bool do_k, bool do_v) __attribute__((always_inline)) {
         // key row behind tile row r
         auto key_of = [&](int r) __attribute__((always_inline)) {
             return t < nband ? min((kt_hi - t) * kTileN + r, N - 1)
@@ -210,6 +209,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
         };
 #pragma unroll
         for (int it = 0; it < NCH; ++it) {
+            if (!do_k) break;
             const int blk = (wave * NCH + it) * 1024;  // wave-uniform LDS block
             const int P = blk + lane * 16;
             const int within = P % (CPR * 256);
@@ -220,6 +220,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
         }
 #pragma unroll
         for (int it = 0; it < NCHV; ++it) {
+            if (!do_v) break;
             const int blk = (wave * NCHV + it) * 1024;
             const int P = blk + lane * 16;
             const int row = P / RBV, inrow = P % RBV;
@@ -238,160 +239,178 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     float m_run = -INFINITY, l_run = 0.f;
     const float c = p.c;
 
-    auto compute_tile = [&](int t, const char* kl, const char* vl) __attribute__((always_inline)) {
-        const bool band = t < nband;
-        const int kt = kt_hi - t;
-        const bool active = wave_live && (band ? (kt <= wkt_hi && (STRIDED || kt >= wkt_lo)) : true);
-        if (active) {
-
-            // S^T for the two 32-key halves of the tile; the lane feeds key
-            // row kb*32 + sigma(l32), stored at position kb*32 + l32
-            f32x16_t s[2];
+    // S^T of tile t from the K buffer kl (the lane feeds key row
+    // kb*32 + sigma(l32), stored at position kb*32 + l32)
+    auto scores = [&](const char* kl, f32x16_t* sc) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+            for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
 #pragma unroll
-                for (int cc = 0; cc < NQF; ++cc) {
-                    if constexpr (BF) {
-                        const bf16x8_t a = *(const bf16x8_t*)(kl + k_lane + ((kb * 2 * CPR + 2 * cc) << 8));
-                        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], s[kb], 0, 0, 0);
-                    } else {
-                        const float a =
-                            *(const float*)(kl + k_lane + ((kb * 2 * CPR + (cc >> 1)) << 8) + ((cc & 1) << 3));
-                        s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[cc], s[kb], 0, 0, 0);
-                    }
+            for (int cc = 0; cc < NQF; ++cc) {
+                if constexpr (BF) {
+                    const bf16x8_t a = *(const bf16x8_t*)(kl + k_lane + ((kb * 2 * CPR + 2 * cc) << 8));
+                    sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], sc[kb], 0, 0, 0);
+                } else {
+                    const float a =
+                        *(const float*)(kl + k_lane + ((kb * 2 * CPR + (cc >> 1)) << 8) + ((cc & 1) << 3));
+                    sc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[cc], sc[kb], 0, 0, 0);
                 }
             }
-
-            // mask: only tiles not entirely inside every row's band
-            const int j0 = kt * kTileN;
-            const bool edge = band ? !(j0 + kTileN - 1 <= qw0 && j0 >= qw0 + kQw - W)
-                                   : ((t - nband + 1) * kTileN > M);
-            if (edge) {
-                // bit o of smask: key j0 + o is a multiple of the stride
-                uint64_t smask = 0;
-                if (STRIDED && band) {
-                    const int r0 = j0 % p.stride;
-                    for (int o = r0 == 0 ? 0 : p.stride - r0; o < kTileN; o += p.stride) smask |= 1ull << o;
-                }
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int r = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
-                        bool ok;
-                        if (band) {
-                            const int j = j0 + r;
-                            const int dist = qi - j;
-                            ok = dist >= 0 && (dist < W || (STRIDED && ((smask >> r) & 1)));
-                        } else {
-                            ok = (t - nband) * kTileN + r < M;
-                        }
-                        if (!ok) s[kb][i] = -INFINITY;
-                    }
-            }
-
-            // online softmax (log2 domain); the lane pair (l, l^32) shares a query
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-            mx = partner_max(mx);
-            // The reference max moves only when the tile max exceeds it by
-            // more than 8 (log2 units): probabilities then stay below 2^8,
-            // which the fp32 sums and the bf16 P operand carry without loss,
-            // and most tiles skip the O / l rescale.  Lanes l and l^32 see the
-            // same max, so they always take the same decision.
-            const float m_cand = fmaxf(m_run, mx * c);
-            const bool grow = m_cand > m_run + 8.f;  // false while both are -inf
-            float alpha = 1.f;
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-                if (grow) {
-                    alpha = __builtin_amdgcn_exp2f(m_run - m_cand);  // 0 on the first finite max
-                    m_run = m_cand;
-                }
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-            }
-            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // row with no allowed key yet
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -m_use));
-
-            // O^T += V^T P^T.  The row sum adds the same probabilities the
-            // product uses: bf16-rounded ones (packed dot with (1, 1)), so
-            // the output is an exact convex combination of V rows.
-            float rs = 0.f;
-            if constexpr (BF) {
-                const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-                for (int c2 = 0; c2 < 4; ++c2) {
-                    // pairs are built as bf16x2 values and only whole vectors are
-                    // bit-cast: extracting a dword of a bf16x8 and bit-casting it
-                    // to bf16x2 mis-compiles (every pair reads element 0).
-                    u32x4_t pw;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const bf16x2_t pr = {(__bf16)s[c2 >> 1][8 * (c2 & 1) + 2 * e],
-                                             (__bf16)s[c2 >> 1][8 * (c2 & 1) + 2 * e + 1]};
-                        rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
-                        pw[e] = __builtin_bit_cast(uint32_t, pr);
-                    }
-                    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        // rows 16*c2 + 8*g + 4*rd + (lane&15)/4, 4 elements at
-                        // d = 32*db + 16*((lane>>4)&1) + 4*(lane&3)
-                        const char* vp = vl + v_lane + 16 * c2 * RBV + 64 * db;
-                        const i16x4_t lo = lds_read_tr16(vp);
-                        const i16x4_t hi = lds_read_tr16(vp + 4 * RBV);
-                        const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
-                        const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
-                        const u32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
-                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8_t, a4), pb, oacc[db], 0, 0, 0);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        rs += s[kb][i];
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db) {
-                            // row kb*32 + 16*(i>>3) + 8*g + (i&7), d = 32*db + l32
-                            const float a = *(const float*)(vl + v_lane +
-                                                            (kb * 32 + 16 * (i >> 3) + (i & 7)) * RBV + 128 * db);
-                            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][i], oacc[db], 0, 0, 0);
-                        }
-                    }
-            }
-            l_run = l_run * alpha + rs;
         }
     };
 
-    // A buffer is refilled only after the barrier that closes the iteration
-    // which last read it.
-    issue_tile(0, kb0, vb0);
+    // mask tile t: only tiles not entirely inside every row of this wave's band
+    auto mask_tile = [&](int t, f32x16_t* sc) __attribute__((always_inline)) {
+        const bool band = t < nband;
+        const int j0 = (kt_hi - t) * kTileN;
+        const bool edge = band ? !(j0 + kTileN - 1 <= qw0 && j0 >= qw0 + kQw - W)
+                               : ((t - nband + 1) * kTileN > M);
+        if (edge) {
+            // bit o of smask: key j0 + o is a multiple of the stride
+            uint64_t smask = 0;
+            if (STRIDED && band) {
+                const int r0 = j0 % p.stride;
+                for (int o = r0 == 0 ? 0 : p.stride - r0; o < kTileN; o += p.stride) smask |= 1ull << o;
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    // non-short-circuit operators: a straight-line select,
+                    // no per-element divergent branches
+                    const int r = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
+                    const int dist = qi - (j0 + r);
+                    const bool in_band = (dist >= 0) & ((dist < W) | (STRIDED & (((smask >> r) & 1ull) != 0)));
+                    const bool in_comp = (t - nband) * kTileN + r < M;
+                    sc[kb][i] = (band ? in_band : in_comp) ? sc[kb][i] : -INFINITY;
+                }
+        }
+    };
+
+    // online softmax of a masked score tile: first the row max and the
+    // (rare) rescale of O, which ends in a branch; the exponentials follow in
+    // softmax_pv, in the same basic block as the next tile's score MFMAs.
+    float alpha = 1.f;
+    auto softmax_head = [&](f32x16_t* sc) __attribute__((always_inline)) {
+        // log2 domain; the lane pair (l, l^32) shares a query
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
+        mx = partner_max(mx);
+        // The reference max moves only when the tile max exceeds it by more
+        // than 8 (log2 units): probabilities then stay below 2^8, which the
+        // fp32 sums and the bf16 P operand carry without loss, and most tiles
+        // skip the O / l rescale.  Lanes l and l^32 see the same max, so they
+        // always take the same decision.
+        const float m_cand = fmaxf(m_run, mx * c);
+        const bool grow = m_cand > m_run + 8.f;  // false while both are -inf
+        alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_cand) : 1.f;  // 0 on the first finite max
+        m_run = grow ? m_cand : m_run;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        }
+    };
+    // exponentials, row sum, then O^T += V^T P^T from vl
+    auto softmax_pv = [&](f32x16_t* sc, const char* vl) __attribute__((always_inline)) {
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // row with no allowed key yet
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], c, -m_use));
+
+        // The row sum adds the same probabilities the product uses:
+        // bf16-rounded ones (packed dot with (1, 1)), so the output is an
+        // exact convex combination of V rows.
+        float rs = 0.f;
+        if constexpr (BF) {
+            const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+            bf16x8_t pb[4];
+#pragma unroll
+            for (int c2 = 0; c2 < 4; ++c2) {
+                // pairs are built as bf16x2 values and only whole vectors are
+                // bit-cast: extracting a dword of a bf16x8 and bit-casting it
+                // to bf16x2 mis-compiles (every pair reads element 0).
+                u32x4_t pw;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bf16x2_t pr = {(__bf16)sc[c2 >> 1][8 * (c2 & 1) + 2 * e],
+                                         (__bf16)sc[c2 >> 1][8 * (c2 & 1) + 2 * e + 1]};
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+                    pw[e] = __builtin_bit_cast(uint32_t, pr);
+                }
+                pb[c2] = __builtin_bit_cast(bf16x8_t, pw);
+            }
+#pragma unroll
+            for (int c2 = 0; c2 < 4; ++c2)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    // rows 16*c2 + 8*g + 4*rd + (lane&15)/4, 4 elements at
+                    // d = 32*db + 16*((lane>>4)&1) + 4*(lane&3)
+                    const char* vp = vl + v_lane + 16 * c2 * RBV + 64 * db;
+                    const i16x4_t lo = lds_read_tr16(vp);
+                    const i16x4_t hi = lds_read_tr16(vp + 4 * RBV);
+                    const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
+                    const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
+                    const u32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a4), pb[c2],
+                                                                      oacc[db], 0, 0, 0);
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    rs += sc[kb][i];
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        // row kb*32 + 16*(i>>3) + 8*g + (i&7), d = 32*db + l32
+                        const float a =
+                            *(const float*)(vl + v_lane + (kb * 32 + 16 * (i >> 3) + (i & 7)) * RBV + 128 * db);
+                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sc[kb][i], oacc[db], 0, 0, 0);
+                    }
+                }
+        }
+        l_run = l_run * alpha + rs;
+    };
+
+    // Two-stage pipeline over the tile list: K runs one tile ahead of V.
+    // Iteration t reads K(t+1) (scores of the next tile, whose matrix work
+    // overlaps this tile's softmax) and V(t), while the copies of K(t+2) and
+    // V(t+1) land in the buffers freed by iteration t-1.  Every wave walks the
+    // whole tile list of its workgroup; tiles outside its own rows' band come
+    // out fully masked.  A buffer is refilled only after the barrier that
+    // closes the iteration which last read it.
+    issue_tile(0, kb0, vb0, true, true);
+    if (ntiles > 1) issue_tile(1, kb1, vb1, true, false);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int t = 0; t < ntiles; t += 2) {
-        if (t + 1 < ntiles) issue_tile(t + 1, kb1, vb1);
-        compute_tile(t, kb0, vb0);
+    f32x16_t scur[2];
+    scores(kb0, scur);
+    mask_tile(0, scur);
+    __syncthreads();
+
+    auto step = [&](int t, const char* kn, const char* vc, char* ki, char* vi) __attribute__((always_inline)) {
+        if (t + 2 < ntiles) issue_tile(t + 2, ki, vi, true, false);
+        if (t + 1 < ntiles) issue_tile(t + 1, ki, vi, false, true);
+        softmax_head(scur);
+        f32x16_t snext[2];
+        scores(kn, snext);  // past the last tile this reads stale data and is discarded
+        softmax_pv(scur, vc);
+        if (t + 1 < ntiles) mask_tile(t + 1, snext);
+        scur[0] = snext[0];
+        scur[1] = snext[1];
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (t + 1 < ntiles) {
-            if (t + 2 < ntiles) issue_tile(t + 2, kb0, vb0);
-            compute_tile(t + 1, kb1, vb1);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-        }
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, kb1, vb0, kb0, vb1);
+        if (t + 1 < ntiles) step(t + 1, kb0, vb1, kb1, vb0);
     }
 
     // ---- epilogue: O / l, lane holds d = 32*db + 8*quad + 4*g + 0..3

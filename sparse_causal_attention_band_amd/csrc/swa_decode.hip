@@ -11,15 +11,22 @@
 // along the slots ("split-K"): grid = (splits, KV heads, sequences), each
 // workgroup streams up to 512 slots of one KV head in 64-slot tiles and
 // serves all G query heads of that KV head, so every K/V byte is read from
-// HBM once.  Per tile:
-//   * K rows are copied HBM -> LDS with 16-byte coalesced loads (double
-//     buffered); V rows go HBM -> registers in the layout the P*V step uses.
-//   * scores: one (head, slot) pair per lane, a full-row dot product from LDS
-//     (bf16 pairs through v_dot2, fp32 through fma);
-//   * online softmax per head across the wave (log2 domain);
-//   * P*V: lane = (16-byte column chunk, row group), fp32 accumulators.
-// The workgroup writes (max, sum, weighted V) per head to the workspace; a
-// second kernel merges the splits by log-sum-exp rescaling.
+// HBM once.  The kernel is a pure register stream:
+//   * a 16-byte chunk per lane, a ring row of d elements spread over CPR
+//     consecutive lanes (one 256-byte bf16 row per 16 lanes: every load
+//     instruction reads 1 KiB of contiguous HBM), a 3-deep ring of tiles in
+//     registers so two more tiles are in flight while one is consumed; the
+//     loads are non-temporal (each byte is read once per step);
+//   * scores: per-lane partial dot products (v_dot2 on bf16 pairs), summed
+//     over the lanes of a row with DPP row permutes;
+//   * each group of lanes sharing a row keeps its own online softmax (max,
+//     sum, weighted V for its d-chunk) -- no barrier and no LDS in the loop;
+//   * P*V: two rows at a time, bf16 V values of the two rows interleaved with
+//     v_perm so one v_dot2 adds both rows' contribution (P rounded to bf16,
+//     and the sum taken over the same rounded P);
+//   * at the end the row groups are merged (log-sum-exp) through LDS, and the
+//     workgroup writes (max, sum, weighted V) per head to the workspace.
+// A second kernel merges the splits by log-sum-exp rescaling.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,29 +40,10 @@ namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
 constexpr int kTile = 64;
-
-// XOR swizzle of 16-byte chunks by row: lane r reads row r, so the 8 lanes
-// served together must hit 8 different chunk columns.
-template <int RB>
-__device__ __forceinline__ int kd_off(int row, int byte) {
-    return row * RB + ((((byte >> 4) ^ (row & 7))) << 4) + (byte & 15);
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
-}
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // Pair E of a bf16x8 value.  Taken with a vector shuffle: bit-casting a dword
 // extracted from a u32x4 to bf16x2 mis-compiles (every pair becomes pair 0).
@@ -64,28 +52,43 @@ __device__ __forceinline__ bf16x2_t pair(bf16x8_t v) {
     return __builtin_shufflevector(v, v, 2 * E, 2 * E + 1);
 }
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Sum over the LANES consecutive lanes that hold one row (LANES = 8, 16 or 32).
+template <int LANES>
+__device__ __forceinline__ float row_sum(float x) {
+    // xor 1 and xor 2 inside quads, then the 8- and 16-lane mirrors (all DPP)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, true));
+    if constexpr (LANES >= 16) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, true));
+    if constexpr (LANES >= 32) x += __shfl_xor(x, 16, 64);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
 
 template <bool BF, int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams p) {
     using elem_t = typename std::conditional<BF, uint16_t, float>::type;
     constexpr int ES = (int)sizeof(elem_t);
     constexpr int RB = D * ES;          // bytes per ring row
-    constexpr int CPR = RB / 16;        // 16-byte chunks per row
+    constexpr int CPR = RB / 16;        // lanes per row (one 16-byte chunk each)
     constexpr int EPC = 16 / ES;        // elements per chunk
-    constexpr int NCH = kTile * CPR / kThreads;   // K chunks per thread per tile
-    constexpr int RG = kThreads / CPR;  // row groups of the P*V layout
-    constexpr int RPT = kTile / RG;     // rows per thread per tile in P*V
-    constexpr int HPW = (G + 3) / 4;    // heads per wave in the score phase
-    static_assert(kTile * CPR % kThreads == 0 && kThreads % CPR == 0, "layout");
+    constexpr int RG = kThreads / CPR;  // row groups per workgroup
+    constexpr int RPT = kTile / RG;     // rows per lane per tile
+    // tiles held in registers (fewer where the row and head count need the room)
+    constexpr int PD = BF ? (G >= 8 ? 2 : 3) : (CPR >= 32 ? 1 : 2);
+    static_assert(CPR == 8 || CPR == 16 || CPR == 32, "row width");
+    static_assert(!BF || RPT % 2 == 0, "rows are paired for v_dot2");
 
-    __shared__ __attribute__((aligned(16))) char kl[2][kTile * RB];
-    __shared__ __attribute__((aligned(16))) u32x4_t ql[G][CPR];      // query rows, raw
-    __shared__ float pl[kTile][G];                                   // probabilities
-    __shared__ float al[G];                                          // per-tile rescale
+    __shared__ float sm_ml[RG][G][2];
+    __shared__ float sm_acc[RG][G][D];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
+    const int dc = tid % CPR, rg = tid / CPR;
     const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int W = p.W;
     const int pb = p.pos[b];
@@ -95,176 +98,187 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     if (s0 >= s1) return;  // nothing valid here; the merge never reads this split
 
     const size_t ring = (size_t)(b * p.Hkv + kvh) * (size_t)W * D;
-    const elem_t* kg = (const elem_t*)p.kring + ring;
-    const elem_t* vg = (const elem_t*)p.vring + ring;
-    const int h0 = kvh * G;  // first query head of this KV head
+    const char* kg = (const char*)((const elem_t*)p.kring + ring) + dc * 16;
+    const char* vg = (const char*)((const elem_t*)p.vring + ring) + dc * 16;
+    const int h0 = kvh * G;
 
-    // query rows -> LDS (sign of the scale folded in exactly)
-    for (int u = tid; u < G * CPR; u += kThreads) {
-        const int hh = u / CPR, ch = u % CPR;
-        u32x4_t w = *(const u32x4_t*)((const char*)p.q + ((size_t)(b * p.Hq + h0 + hh) * D) * ES + ch * 16);
+    // this lane's 16-byte chunk of every query row (sign of the scale folded in)
+    u32x4_t qc[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        u32x4_t w = *(const u32x4_t*)((const char*)p.q + ((size_t)(b * p.Hq + h0 + hh) * D) * ES + dc * 16);
         if (p.neg) w ^= (BF ? 0x80008000u : 0x80000000u);
-        ql[hh][ch] = w;
+        qc[hh] = w;
     }
 
     const int ntile = (s1 - s0 + kTile - 1) / kTile;
-    u32x4_t kr[NCH], vr[RPT], vn[RPT];
-    auto load_k = [&](int t) {
-        const int base = s0 + t * kTile;
-#pragma unroll
-        for (int it = 0; it < NCH; ++it) {
-            const int u = tid + kThreads * it;
-            const int row = u / CPR, ch = u % CPR;
-            u32x4_t w = {0u, 0u, 0u, 0u};
-            if (base + row < s1) w = *(const u32x4_t*)((const char*)(kg + (size_t)(base + row) * D) + ch * 16);
-            kr[it] = w;
-        }
-    };
-    auto store_k = [&](int buf) {
-#pragma unroll
-        for (int it = 0; it < NCH; ++it) {
-            const int u = tid + kThreads * it;
-            const int row = u / CPR, ch = u % CPR;
-            *(u32x4_t*)(kl[buf] + kd_off<RB>(row, ch * 16)) = kr[it];
-        }
-    };
-    const int dc = tid % CPR, rg = tid / CPR;
-    auto load_v = [&](int t, u32x4_t* dst) {
-        const int base = s0 + t * kTile;
+    u32x4_t kr[PD][RPT], vr[PD][RPT];
+    auto load = [&](int t, u32x4_t* kd, u32x4_t* vd) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < RPT; ++k) {
-            const int row = rg + RG * k;
-            u32x4_t w = {0u, 0u, 0u, 0u};
-            if (base + row < s1) w = *(const u32x4_t*)((const char*)(vg + (size_t)(base + row) * D) + dc * 16);
-            dst[k] = w;
+            const int slot = s0 + t * kTile + rg + RG * k;
+            u32x4_t kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
+            if (t < ntile && slot < s1) {
+                // read once per step: non-temporal loads stream past the caches
+                kw = __builtin_nontemporal_load((const u32x4_t*)(kg + (size_t)slot * RB));
+                vw = __builtin_nontemporal_load((const u32x4_t*)(vg + (size_t)slot * RB));
+            }
+            kd[k] = kw;
+            vd[k] = vw;
         }
     };
 
-    float m_h[HPW], l_h[HPW];
+    float m_h[G], l_h[G], acc[G][EPC];
 #pragma unroll
-    for (int k = 0; k < HPW; ++k) { m_h[k] = -INFINITY; l_h[k] = 0.f; }
-    float acc[G][EPC];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
+    for (int hh = 0; hh < G; ++hh) {
+        m_h[hh] = -INFINITY;
+        l_h[hh] = 0.f;
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[hh][e] = 0.f;
+    }
+    const float c = p.c;
 
-    load_k(0);
-    load_v(0, vr);
-    store_k(0);
-    __syncthreads();
-
-    for (int t = 0; t < ntile; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntile) {
-            load_k(t + 1);
-            load_v(t + 1, vn);
-        }
-        // ---- scores and softmax: wave w owns heads w, w+4, ...
-        const int base = s0 + t * kTile;
-#pragma unroll
-        for (int k = 0; k < HPW; ++k) {
-            const int hh = wave + 4 * k;
-            if (hh < G) {
-                float dot = 0.f;
-#pragma unroll
-                for (int ch = 0; ch < CPR; ++ch) {
-                    const u32x4_t kw = *(const u32x4_t*)(kl[buf] + kd_off<RB>(lane, ch * 16));
-                    const u32x4_t qw = ql[hh][ch];
-                    if constexpr (BF) {
-                        const bf16x8_t k8 = __builtin_bit_cast(bf16x8_t, kw);
-                        const bf16x8_t q8 = __builtin_bit_cast(bf16x8_t, qw);
-                        dot = __builtin_amdgcn_fdot2_f32_bf16(pair<0>(k8), pair<0>(q8), dot, false);
-                        dot = __builtin_amdgcn_fdot2_f32_bf16(pair<1>(k8), pair<1>(q8), dot, false);
-                        dot = __builtin_amdgcn_fdot2_f32_bf16(pair<2>(k8), pair<2>(q8), dot, false);
-                        dot = __builtin_amdgcn_fdot2_f32_bf16(pair<3>(k8), pair<3>(q8), dot, false);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) dot = fmaf(__uint_as_float(kw[e]), __uint_as_float(qw[e]), dot);
-                    }
-                }
-                const float s = (base + lane < s1) ? dot * p.c : -INFINITY;
-                const float m_new = fmaxf(m_h[k], wave_max(s));
-                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = __builtin_amdgcn_exp2f(m_h[k] - m_use);
-                const float e = __builtin_amdgcn_exp2f(s - m_use);
-                m_h[k] = m_new;
-                l_h[k] = l_h[k] * alpha + e;
-                pl[lane][hh] = e;
-                if (lane == 0) al[hh] = alpha;
-            }
-        }
-        __syncthreads();
-        // ---- P*V
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const float a = al[hh];
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[hh][e] *= a;
-        }
+    auto consume = [&](int t, const u32x4_t* kd, const u32x4_t* vd) __attribute__((always_inline)) {
+        // scores of this lane's RPT rows for every head (log2 domain)
+        float sc[G][RPT];
 #pragma unroll
         for (int k = 0; k < RPT; ++k) {
-            const int row = rg + RG * k;
-            float vv[EPC];
-            if constexpr (BF) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vv[2 * e] = bf_lo(vr[k][e]);
-                    vv[2 * e + 1] = bf_hi(vr[k][e]);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vv[e] = __uint_as_float(vr[k][e]);
-            }
+            const bool valid = s0 + t * kTile + rg + RG * k < s1;
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) {
-                const float pr = pl[row][hh];
+                float part = 0.f;
+                if constexpr (BF) {
+                    const bf16x8_t k8 = __builtin_bit_cast(bf16x8_t, kd[k]);
+                    const bf16x8_t q8 = __builtin_bit_cast(bf16x8_t, qc[hh]);
+                    part = __builtin_amdgcn_fdot2_f32_bf16(pair<0>(k8), pair<0>(q8), part, false);
+                    part = __builtin_amdgcn_fdot2_f32_bf16(pair<1>(k8), pair<1>(q8), part, false);
+                    part = __builtin_amdgcn_fdot2_f32_bf16(pair<2>(k8), pair<2>(q8), part, false);
+                    part = __builtin_amdgcn_fdot2_f32_bf16(pair<3>(k8), pair<3>(q8), part, false);
+                } else {
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) acc[hh][e] = fmaf(pr, vv[e], acc[hh][e]);
+                    for (int e = 0; e < 4; ++e) part = fmaf(__uint_as_float(kd[k][e]), __uint_as_float(qc[hh][e]), part);
+                }
+                const float dot = row_sum<CPR>(part);
+                sc[hh][k] = valid ? dot * c : -INFINITY;
             }
         }
-        if (t + 1 < ntile) {
-            store_k(buf ^ 1);
+        // online softmax per head for this row group; the reference max moves
+        // only when it grows by more than 8 (log2 units), so most tiles skip
+        // the rescale of acc (probabilities stay below 2^8)
+        bool grow_any = false;
+        float alpha[G];
 #pragma unroll
-            for (int k = 0; k < RPT; ++k) vr[k] = vn[k];
+        for (int hh = 0; hh < G; ++hh) {
+            float mx = sc[hh][0];
+#pragma unroll
+            for (int k = 1; k < RPT; ++k) mx = fmaxf(mx, sc[hh][k]);
+            const float m_cand = fmaxf(m_h[hh], mx);
+            const bool grow = m_cand > m_h[hh] + 8.f;
+            alpha[hh] = grow ? __builtin_amdgcn_exp2f(m_h[hh] - m_cand) : 1.f;
+            m_h[hh] = grow ? m_cand : m_h[hh];
+            grow_any |= grow;
         }
-        __syncthreads();
+        if (__builtin_amdgcn_ballot_w64(grow_any) != 0) {
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                l_h[hh] *= alpha[hh];
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) acc[hh][e] *= alpha[hh];
+            }
+        }
+        if constexpr (BF) {
+            const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+            for (int k = 0; k < RPT; k += 2) {
+                // V values of rows k and k+1 interleaved per element
+                uint32_t lo[4], hi[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    lo[e] = __builtin_amdgcn_perm(vd[k + 1][e], vd[k][e], 0x05040100u);
+                    hi[e] = __builtin_amdgcn_perm(vd[k + 1][e], vd[k][e], 0x07060302u);
+                }
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) {
+                    const float mu = (m_h[hh] == -INFINITY) ? 0.f : m_h[hh];
+                    const bf16x2_t pp = {(__bf16)__builtin_amdgcn_exp2f(sc[hh][k] - mu),
+                                         (__bf16)__builtin_amdgcn_exp2f(sc[hh][k + 1] - mu)};
+                    l_h[hh] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_h[hh], false);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[hh][2 * e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lo[e]), pp,
+                                                                         acc[hh][2 * e], false);
+                        acc[hh][2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hi[e]), pp,
+                                                                             acc[hh][2 * e + 1], false);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < RPT; ++k)
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) {
+                    const float mu = (m_h[hh] == -INFINITY) ? 0.f : m_h[hh];
+                    const float pr = __builtin_amdgcn_exp2f(sc[hh][k] - mu);
+                    l_h[hh] += pr;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[hh][e] = fmaf(pr, __uint_as_float(vd[k][e]), acc[hh][e]);
+                }
+        }
+    };
+
+    // register ring: tiles t, t+1, ..., t+PD-1 are loaded before tile t is used
+#pragma unroll
+    for (int j = 0; j < PD; ++j) load(j, kr[j], vr[j]);
+    for (int t = 0; t < ntile; t += PD) {
+#pragma unroll
+        for (int j = 0; j < PD; ++j) {
+            if (t + j < ntile) {
+                consume(t + j, kr[j], vr[j]);
+                load(t + j + PD, kr[j], vr[j]);
+            }
+        }
     }
 
-    // ---- reduce the row groups: first inside the wave (lanes with the same
-    // chunk), then across the 4 waves through LDS (reusing the K buffers).
+    // ---- merge the row groups: per head M = max m, weights 2^(m - M)
+    const int lane_in_row = dc;
+    if (lane_in_row == 0) {
 #pragma unroll
-    for (int o = CPR; o < 64; o <<= 1)
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[hh][e] += __shfl_xor(acc[hh][e], o, 64);
-    float* red = (float*)&kl[0][0];  // [4 waves][G][D] floats
-    static_assert(4 * G * D * 4 <= 2 * kTile * RB, "reduction buffer");
-    if (lane < CPR) {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) red[(wave * G + hh) * D + lane * EPC + e] = acc[hh][e];
-    }
-    const size_t part = ((size_t)(b * p.Hq + h0) * p.nsplit + split);  // head hh adds hh * nsplit
-#pragma unroll
-    for (int k = 0; k < HPW; ++k) {
-        const int hh = wave + 4 * k;
-        if (hh < G) {
-            const float l = wave_sum(l_h[k]);
-            if (lane == 0) {
-                p.ws_ml[(part + (size_t)hh * p.nsplit) * 2 + 0] = m_h[k];
-                p.ws_ml[(part + (size_t)hh * p.nsplit) * 2 + 1] = l;
-            }
+        for (int hh = 0; hh < G; ++hh) {
+            sm_ml[rg][hh][0] = m_h[hh];
+            sm_ml[rg][hh][1] = l_h[hh];
         }
     }
     __syncthreads();
+    float wgt[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) M = fmaxf(M, sm_ml[r][hh][0]);
+        wgt[hh] = (m_h[hh] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_h[hh] - M);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) sm_acc[rg][hh][dc * EPC + e] = acc[hh][e] * wgt[hh];
+    }
+    __syncthreads();
+    const size_t part = ((size_t)(b * p.Hq + h0) * p.nsplit + split);  // head hh adds hh * nsplit
     for (int u = tid; u < G * D; u += kThreads) {
         const int hh = u / D, d = u % D;
-        const float s = red[(0 * G + hh) * D + d] + red[(1 * G + hh) * D + d] + red[(2 * G + hh) * D + d] +
-                        red[(3 * G + hh) * D + d];
-        p.ws_acc[(part + (size_t)hh * p.nsplit) * D + d] = s;
+        float a = 0.f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) a += sm_acc[r][hh][d];
+        p.ws_acc[(part + (size_t)hh * p.nsplit) * D + d] = a;
+    }
+    if (tid < G) {
+        const int hh = tid;
+        float M = -INFINITY;
+        for (int r = 0; r < RG; ++r) M = fmaxf(M, sm_ml[r][hh][0]);
+        float L = 0.f;
+        for (int r = 0; r < RG; ++r) {
+            const float m = sm_ml[r][hh][0];
+            if (m != -INFINITY) L += sm_ml[r][hh][1] * __builtin_amdgcn_exp2f(m - M);
+        }
+        p.ws_ml[(part + (size_t)hh * p.nsplit) * 2 + 0] = M;
+        p.ws_ml[(part + (size_t)hh * p.nsplit) * 2 + 1] = L;
     }
 }
 
