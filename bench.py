@@ -212,7 +212,8 @@ def main():
         # cache-resident ring
         rings = [(dkr.to(dev), dvr.to(dev)), (dkr.to(dev), dvr.to(dev))]
         dout = torch.empty_like(dqd)
-        ws = torch.empty(swa.decode_workspace_bytes(B, Hq, Hkv, d, W), dtype=torch.uint8, device=dev)
+        need = swa.decode_workspace_bytes(B, Hq, Hkv, d, W)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
 
         def dstep(i=0):
             kr_, vr_ = rings[i % 2]
@@ -226,7 +227,7 @@ def main():
         line["decode"] = {"workload": dcfg.name, "value": round(gbs, 1), "unit": "GB/s",
                           "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "avg_step_ms": round(dms, 4),
                           "algorithmic_bytes_per_step": dbytes,
-                          "kernels": "decode_split_kernel<bf16,128,4> + decode_merge_kernel",
+                          "kernels": "decode_split_kernel<bf16,128,4> (one split: no merge kernel)",
                           "cpu_baseline": None if dec_cpu_s is None else
                           {"value": round(dbytes / dec_cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1,
                            "kind": "oracle", "sample": f"whole {dcfg.name} step, float64 numpy, {dec_cpu_s:.2f} s"}}

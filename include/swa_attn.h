@@ -95,10 +95,14 @@ SWA_API int swa_attn_fwd_f32(const float* q, const float* k, const float* v, flo
  *   workspace    : device scratch of at least
  *                  swa_decode_workspace_bytes(B, Hq, Hkv, d, window) bytes,
  *                  16-byte aligned; its contents on entry do not matter.
+ *                  When that size is 0 the pointer is not used (may be NULL).
  *   Hq / Hkv must be 1, 2, 4 or 8; d in {64, 128}; window >= 1.
- * Two kernels run: a split-K pass that streams K/V slots from HBM and writes
- * per-split (max, sum, weighted V) partials into the workspace, then a
- * log-sum-exp merge of the splits that writes `out`.
+ * One workgroup streams the K/V slots of one (sequence, KV head) pair from
+ * HBM and serves its Hq/Hkv query heads.  With fewer than 512 such pairs the
+ * slots are split so the GPU still gets two workgroups per CU: each split
+ * writes (max, sum, weighted V) partials into the workspace and a second
+ * kernel merges them by log-sum-exp; with 512 or more pairs there is one
+ * kernel and no workspace.
  */
 SWA_API int swa_decode(const void* q, const void* kring, const void* vring, const int32_t* pos,
                void* out, int B, int Hq, int Hkv, int d, float scale,
@@ -109,7 +113,8 @@ SWA_API int swa_decode_f32(const float* q, const float* kring, const float* vrin
                    float* out, int B, int Hq, int Hkv, int d, float scale,
                    void* workspace, size_t workspace_bytes, int window, hipStream_t stream);
 
-/* Workspace bytes swa_decode / swa_decode_f32 need; 0 for invalid sizes. */
+/* Workspace bytes swa_decode / swa_decode_f32 need (0 when the split plan
+   for these sizes has one split, and for invalid sizes). */
 SWA_API size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window);
 
 /* Message for the last non-zero return on the calling thread ("" if none). */

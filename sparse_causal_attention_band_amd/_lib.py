@@ -149,14 +149,15 @@ def decode(q: torch.Tensor, kring: torch.Tensor, vring: torch.Tensor, pos: torch
         out = torch.empty_like(q)
     _need(out, "out", dtype, dev)
     need = decode_workspace_bytes(B, Hq, kring.shape[1], d, W)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    if workspace.device != dev or not workspace.is_contiguous():
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous tensor on the same GPU")
+    ws_ptr = 0 if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     fn = lib().swa_decode if dtype == torch.bfloat16 else lib().swa_decode_f32
     _check(fn(q.data_ptr(), kring.data_ptr(), vring.data_ptr(), pos.data_ptr(), out.data_ptr(),
-              B, Hq, kring.shape[1], d, float(scale), workspace.data_ptr(),
-              workspace.numel() * workspace.element_size(), W, _stream(dev)))
+              B, Hq, kring.shape[1], d, float(scale), ws_ptr, ws_bytes, W, _stream(dev)))
     return out

@@ -105,12 +105,13 @@ int decode(bool bf16, const void* q, const void* kring, const void* vring, const
     const int G = Hq / Hkv;
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(SWA_ERR_UNSUPPORTED, "%s: Hq/Hkv = %d not built (1, 2, 4 or 8)", name, G);
-    if (!aligned16(q) || !aligned16(kring) || !aligned16(vring) || !aligned16(out) || !aligned16(workspace))
-        return fail(SWA_ERR_INVALID_ARG, "%s: q, kring, vring, out, workspace must be non-null and 16-byte aligned",
-                    name);
+    if (!aligned16(q) || !aligned16(kring) || !aligned16(vring) || !aligned16(out))
+        return fail(SWA_ERR_INVALID_ARG, "%s: q, kring, vring, out must be non-null and 16-byte aligned", name);
     if (pos == nullptr || ((uintptr_t)pos & 3u)) return fail(SWA_ERR_INVALID_ARG, "%s: pos must be non-null, 4-byte aligned", name);
     if (int rc = check_scale(name, scale)) return rc;
-    const size_t need = swa::decode_workspace_bytes(B, Hq, window, d);
+    const size_t need = swa::decode_workspace_bytes(B, Hq, Hkv, window, d);
+    if (need > 0 && !aligned16(workspace))
+        return fail(SWA_ERR_INVALID_ARG, "%s: workspace must be non-null and 16-byte aligned", name);
     if (workspace_bytes < need)
         return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes is below the %zu needed", name, workspace_bytes,
                     need);
@@ -124,8 +125,9 @@ int decode(bool bf16, const void* q, const void* kring, const void* vring, const
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.W = window;
-    p.split_len = swa::kDecodeSplit;
-    p.nsplit = (window + p.split_len - 1) / p.split_len;
+    const swa::DecodeSplit plan = swa::decode_split_plan(B, Hkv, window);
+    p.split_len = plan.split_len;
+    p.nsplit = plan.nsplit;
     p.ws_acc = (float*)workspace;
     p.ws_ml = p.ws_acc + (size_t)B * Hq * p.nsplit * d;
     p.c = fabsf(scale) * kLog2e;
@@ -164,7 +166,7 @@ int swa_decode_f32(const float* q, const float* kring, const float* vring, const
 
 size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || window < 1 || (d != 64 && d != 128)) return 0;
-    return swa::decode_workspace_bytes(B, Hq, window, d);
+    return swa::decode_workspace_bytes(B, Hq, Hkv, window, d);
 }
 
 const char* swa_last_error(void) { return g_last_error.c_str(); }

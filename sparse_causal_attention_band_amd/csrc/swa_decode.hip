@@ -8,10 +8,12 @@
 // order; which slots are valid is all that depends on pos.
 //
 // The step is bound by HBM bandwidth (about 4 flops per byte), so it is split
-// along the slots ("split-K"): grid = (splits, KV heads, sequences), each
-// workgroup streams up to 512 slots of one KV head in 64-slot tiles and
-// serves all G query heads of that KV head, so every K/V byte is read from
-// HBM once.  The kernel is a pure register stream:
+// along the slots ("split-K") only as far as needed to give every CU two
+// workgroups: grid = (splits, KV heads, sequences), each workgroup streams
+// its slots of one KV head in 64-slot tiles and serves all G query heads of
+// that KV head, so every K/V byte is read from HBM once.  With one split
+// (512 or more (sequence, KV head) pairs) the workgroup writes the output
+// itself.  The kernel is a pure register stream:
 //   * a 16-byte chunk per lane, a ring row of d elements spread over CPR
 //     consecutive lanes (one 256-byte bf16 row per 16 lanes: every load
 //     instruction reads 1 KiB of contiguous HBM), a 3-deep ring of tiles in
@@ -26,7 +28,7 @@
 //     and the sum taken over the same rounded P);
 //   * at the end the row groups are merged (log-sum-exp) through LDS, and the
 //     workgroup writes (max, sum, weighted V) per head to the workspace.
-// A second kernel merges the splits by log-sum-exp rescaling.
+// With several splits a second kernel merges them by log-sum-exp rescaling.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -95,7 +97,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     const int n = pb <= 0 ? 0 : min(pb, W);
     const int s0 = split * p.split_len;
     const int s1 = min(n, s0 + p.split_len);
-    if (s0 >= s1) return;  // nothing valid here; the merge never reads this split
+    if (s0 >= s1) {
+        // nothing valid here: the merge never reads this split; without a
+        // merge (one split) this is a pos <= 0 row, which is all zeros
+        if (p.nsplit == 1)
+            for (int u = tid; u < G * D; u += kThreads)
+                ((elem_t*)p.out)[(size_t)(b * p.Hq + kvh * G + u / D) * D + u % D] = (elem_t)0;
+        return;
+    }
 
     const size_t ring = (size_t)(b * p.Hkv + kvh) * (size_t)W * D;
     const char* kg = (const char*)((const elem_t*)p.kring + ring) + dc * 16;
@@ -260,6 +269,29 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
         for (int e = 0; e < EPC; ++e) sm_acc[rg][hh][dc * EPC + e] = acc[hh][e] * wgt[hh];
     }
     __syncthreads();
+    if (p.nsplit == 1) {
+        // the only split: normalise and write the output row directly
+        for (int u = tid; u < G * D; u += kThreads) {
+            const int hh = u / D, d = u % D;
+            float M = -INFINITY;
+            for (int r = 0; r < RG; ++r) M = fmaxf(M, sm_ml[r][hh][0]);
+            float a = 0.f, L = 0.f;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                a += sm_acc[r][hh][d];
+                const float m = sm_ml[r][hh][0];
+                if (m != -INFINITY) L += sm_ml[r][hh][1] * __builtin_amdgcn_exp2f(m - M);
+            }
+            elem_t* out = (elem_t*)p.out + (size_t)(b * p.Hq + h0 + hh) * D + d;
+            if constexpr (BF) {
+                const __bf16 x = (__bf16)(a / L);
+                *out = __builtin_bit_cast(uint16_t, x);
+            } else {
+                *out = a / L;
+            }
+        }
+        return;
+    }
     const size_t part = ((size_t)(b * p.Hq + h0) * p.nsplit + split);  // head hh adds hh * nsplit
     for (int u = tid; u < G * D; u += kThreads) {
         const int hh = u / D, d = u % D;
@@ -318,7 +350,7 @@ template <bool BF, int D, int G>
 hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
     hipLaunchKernelGGL((decode_split_kernel<BF, D, G>), dim3(p.nsplit, p.Hkv, p.B), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || p.nsplit == 1) return e;
     hipLaunchKernelGGL((decode_merge_kernel<BF, D>), dim3(p.B * p.Hq), dim3(128), 0, s, p);
     return hipGetLastError();
 }
@@ -340,9 +372,23 @@ hipError_t launch_decode(bool bf16, int d, int G, const DecodeParams& p, hipStre
     return d == 128 ? launch_d<false, 128>(G, p, s) : launch_d<false, 64>(G, p, s);
 }
 
-size_t decode_workspace_bytes(int B, int Hq, int W, int d) {
-    const size_t nsplit = (size_t)(W + kDecodeSplit - 1) / kDecodeSplit;
-    return (size_t)B * Hq * nsplit * ((size_t)d + 2) * sizeof(float);
+DecodeSplit decode_split_plan(int B, int Hkv, int W) {
+    const long long pairs = (long long)B * Hkv;      // (sequence, KV head) pairs
+    const long long want = 512;                       // two workgroups per CU
+    const int tiles = (W + kTile - 1) / kTile;
+    long long ns = pairs >= want ? 1 : (want + pairs - 1) / pairs;
+    if (ns > tiles) ns = tiles;
+    const int tiles_per_split = (int)((tiles + ns - 1) / ns);
+    DecodeSplit sp;
+    sp.split_len = tiles_per_split * kTile;
+    sp.nsplit = (W + sp.split_len - 1) / sp.split_len;
+    return sp;
+}
+
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int W, int d) {
+    const DecodeSplit sp = decode_split_plan(B, Hkv, W);
+    if (sp.nsplit == 1) return 0;
+    return (size_t)B * Hq * sp.nsplit * ((size_t)d + 2) * sizeof(float);
 }
 
 }  // namespace swa

@@ -44,16 +44,22 @@ struct DecodeParams {
     float* ws_acc;   // [B, Hq, nsplit, d]  un-normalised weighted V sums
     float* ws_ml;    // [B, Hq, nsplit, 2]  (running max in log2 units, sum)
     int B, Hq, Hkv, W;
-    int nsplit;      // ceil(W / split_len)
+    int nsplit;      // ceil(W / split_len); 1 = the split kernel writes out itself
     int split_len;   // ring slots per split (multiple of the 64-slot tile)
     float c;         // |scale| * log2(e)
     int neg;
 };
 
-constexpr int kDecodeSplit = 512;
+// Split plan: enough workgroups for two per CU (256 CUs), each split a whole
+// number of 64-slot tiles.  One split means no workspace and no merge kernel.
+struct DecodeSplit {
+    int nsplit;
+    int split_len;
+};
+DecodeSplit decode_split_plan(int B, int Hkv, int W);
 
 hipError_t launch_decode(bool bf16, int d, int G, const DecodeParams& p, hipStream_t s);
 
-size_t decode_workspace_bytes(int B, int Hq, int W, int d);
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int W, int d);
 
 }  // namespace swa

@@ -64,9 +64,10 @@ def test_fwd_rejects_bad_arguments(kw, code):
 
 
 def _dec(**kw):
-    ws = swa.lib().swa_decode_workspace_bytes(2, 8, 2, 128, 64)
+    ws = swa.lib().swa_decode_workspace_bytes(2, 8, 2, 128, 4096)
+    assert ws > 0  # this shape is split, so it needs a workspace
     args = dict(q=A, kr=A * 2, vr=A * 3, pos=A * 4, out=A * 5, B=2, Hq=8, Hkv=2, d=128, scale=0.1,
-                ws=A * 6, wsb=ws, window=64, stream=None)
+                ws=A * 6, wsb=ws, window=4096, stream=None)
     args.update(kw)
     return swa.lib().swa_decode(args["q"], args["kr"], args["vr"], args["pos"], args["out"], args["B"],
                                 args["Hq"], args["Hkv"], args["d"], args["scale"], args["ws"], args["wsb"],
@@ -85,10 +86,13 @@ def test_decode_rejects_bad_arguments(kw, code):
 
 def test_workspace_size_formula():
     L = swa.lib()
-    # splits of 512 slots; per (sequence, query head, split): d floats + (max, sum)
-    assert L.swa_decode_workspace_bytes(64, 32, 8, 128, 4096) == 64 * 32 * 8 * (128 + 2) * 4
-    assert L.swa_decode_workspace_bytes(1, 1, 1, 64, 1) == 1 * 1 * 1 * 66 * 4
-    assert L.swa_decode_workspace_bytes(1, 1, 1, 64, 513) == 2 * 66 * 4
+    # 512 or more (sequence, KV head) pairs: one split, no workspace
+    assert L.swa_decode_workspace_bytes(64, 32, 8, 128, 4096) == 0
+    assert L.swa_decode_workspace_bytes(1, 1, 1, 64, 1) == 0  # a single 64-slot tile cannot split
+    # otherwise ceil(512 / pairs) splits of whole 64-slot tiles, each holding
+    # d floats + (max, sum) per (sequence, query head)
+    assert L.swa_decode_workspace_bytes(1, 1, 1, 64, 513) == 9 * 66 * 4       # 9 tiles, 9 splits
+    assert L.swa_decode_workspace_bytes(10, 32, 8, 128, 4096) == 10 * 32 * 7 * 130 * 4  # 80 pairs -> 7 splits
     assert L.swa_decode_workspace_bytes(1, 3, 2, 64, 8) == 0
     assert L.swa_decode_workspace_bytes(1, 2, 1, 100, 8) == 0
 

@@ -334,6 +334,26 @@ def test_decode_forced_positions_and_nan_slots():
     assert (out[6:8].float() == 0).all()
 
 
+def test_decode_one_split_forced_positions():
+    """64 sequences x 8 KV heads: one split, the workgroup writes the output
+    itself (no workspace, no merge), including pos <= 0 rows."""
+    cfg = inputs.DECODE
+    say("decode one-split path, forced positions")
+    q, kr, vr, pos = inputs.decode_inputs(cfg)
+    forced = [1, 2, 4095, 4096, 4097, 131072, 0, -5, 63, 64, 65]
+    pos[:len(forced)] = torch.tensor(forced, dtype=torch.int32)
+    for b, p_ in enumerate(pos.tolist()):
+        if 0 < p_ < cfg.window:
+            kr[b, :, p_:] = float("nan")
+            vr[b, :, p_:] = float("nan")
+    assert swa.decode_workspace_bytes(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.window) == 0
+    out = swa.decode(q.to(DEV), kr.to(DEV), vr.to(DEV), pos.to(DEV))
+    torch.cuda.synchronize()
+    want = oracle.decode(f64(q), f64(kr), f64(vr), pos.numpy(), cfg.window, 1 / math.sqrt(cfg.d))
+    check_bf16(out, want, "one split")
+    assert (out[6:8].float() == 0).all()
+
+
 @pytest.mark.parametrize("G,d,dtype,W", [(1, 64, "bf16", 100), (2, 128, "bf16", 1500), (8, 64, "bf16", 777),
                                          (4, 128, "f32", 600), (8, 128, "f32", 64), (1, 64, "f32", 1)])
 def test_decode_variants(G, d, dtype, W):
