@@ -12,4 +12,6 @@ from .swa_oracle import (  # noqa: F401
     attn_fwd_parallel,
     decode,
     ring_slot,
+    ring_append,
+    chunk_prefill,
 )

@@ -24,6 +24,10 @@ Everything here is the plain definition, written out in float64 with numpy:
 * The rolling decode cache stores absolute position t (1-based) in slot
   (t-1) mod W (SWA page, §4.2); slot order is not time order, so the oracle
   gathers the valid slots back into time order before attending.
+* Chunked prefill (SWA page, §4.3): the rows of a new chunk need different
+  windows, so each row attends to the cached history in the ring plus the
+  chunk's own earlier rows, under the same band; the history is read before
+  the chunk is written into the ring.
 
 Readings where the pages leave a step open (each one is also listed in the
 design notes of the repository):
@@ -55,6 +59,8 @@ __all__ = [
     "decode",
     "ring_slot",
     "attn_fwd_parallel",
+    "ring_append",
+    "chunk_prefill",
 ]
 
 
@@ -285,4 +291,61 @@ def decode(q, kring, vring, pos, window: int, scale: Optional[float] = None) -> 
             s = scale * (kk @ q[b, h])
             e = np.exp(s - s.max())
             out[b, h] = (e / e.sum()) @ vv
+    return out
+
+
+def ring_append(kring, vring, k, v, p0, window: int):
+    """Write a chunk's K/V rows into the rolling cache (SWA page §4.2).
+
+    kring, vring: [B, Hkv, W, d]; k, v: [B, Hkv, T, d]; p0: [B] number of
+    positions already cached.  Chunk row r is absolute position p0 + r + 1
+    and goes to slot (p0 + r) mod W; later rows overwrite earlier ones.
+    Returns new float64 rings.
+    """
+    kr = np.array(kring, dtype=np.float64, copy=True)
+    vr = np.array(vring, dtype=np.float64, copy=True)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    for b in range(kr.shape[0]):
+        for r in range(k.shape[2]):
+            slot = ring_slot(int(p0[b]) + r + 1, window)
+            kr[b, :, slot] = k[b, :, r]
+            vr[b, :, slot] = v[b, :, r]
+    return kr, vr
+
+
+def chunk_prefill(q, k, v, kring, vring, p0, window: int, scale: Optional[float] = None) -> np.ndarray:
+    """Attention of a chunk of T new tokens over the ring history plus the
+    chunk itself (SWA page §4.3), float64 [B, Hq, T, d].
+
+    q: [B, Hq, T, d]; k, v: [B, Hkv, T, d] (the chunk's own keys/values);
+    kring, vring: [B, Hkv, W, d] holding positions up to p0[b] (not yet the
+    chunk); p0: [B].  Chunk row r is absolute position i = p0 + r + 1 and
+    reads positions max(1, i-W+1) .. i: the history part comes from the ring
+    (position t in slot (t-1) mod W), the rest from the chunk.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    kring = np.asarray(kring, dtype=np.float64)
+    vring = np.asarray(vring, dtype=np.float64)
+    B, Hq, T, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    G = Hq // k.shape[1]
+    out = np.empty((B, Hq, T, v.shape[3]), dtype=np.float64)
+    for b in range(B):
+        start = int(p0[b])
+        n_hist = min(start, window - 1)  # older positions are outside every chunk row's window
+        times = range(start - n_hist + 1, start + 1)
+        slots = np.asarray([ring_slot(t, window) for t in times], dtype=np.int64)
+        # the history in time order, then the chunk: one sequence whose last T
+        # rows are the chunk's rows, each with its full window available
+        for h in range(Hq):
+            g = h // G
+            kk = np.concatenate([kring[b, g][slots], k[b, g]])
+            vv = np.concatenate([vring[b, g][slots], v[b, g]])
+            qq = np.concatenate([np.zeros((n_hist, d)), q[b, h]])
+            rows = np.arange(n_hist, n_hist + T, dtype=np.int64)
+            out[b, h] = _head_rows(qq, kk, vv, rows, window, 0, scale)
     return out

@@ -287,6 +287,74 @@ def test_decode_nonpositive_pos_is_zero():
     assert (out == 0).all()
 
 
+# ---------------------------------------------------------------- chunked prefill
+def test_ring_append_places_positions_like_the_page():
+    """Appending positions 1..5 of the worked example to a 3-slot ring leaves
+    positions 3, 4, 5 in slots 2, 0, 1 (SWA page §4.2)."""
+    g, k, v = _worked()
+    kr = np.zeros((1, 1, 3, 1))
+    vr = np.zeros((1, 1, 3, 1))
+    # two chunks: positions 1..2, then 3..5
+    kr, vr = oracle.ring_append(kr, vr, k[:2].reshape(1, 1, 2, 1), v[:2].reshape(1, 1, 2, 1), [0], 3)
+    kr, vr = oracle.ring_append(kr, vr, k[2:].reshape(1, 1, 3, 1), v[2:].reshape(1, 1, 3, 1), [2], 3)
+    assert list(kr[0, 0, :, 0]) == [k[3], k[4], k[2]]
+    assert list(vr[0, 0, :, 0]) == [v[3], v[4], v[2]]
+
+
+@pytest.mark.parametrize("W,chunks", [(8, [3, 5, 1, 9, 4]), (16, [40, 1, 17]), (5, [1, 1, 1, 2, 13]), (64, [30, 50])])
+def test_chunked_prefill_equals_whole_prefill(W, chunks):
+    """Prefill chunk by chunk over the rolling cache (attend, then append)
+    gives the rows of one whole-sequence prefill (SWA page §4.3): the
+    history read from the ring plus the chunk with the per-row band."""
+    B, Hq, Hkv, d = 2, 4, 2, 6
+    L = sum(chunks)
+    rng = np.random.default_rng(W + L)
+    q = rng.standard_normal((B, Hq, L, d))
+    k = rng.standard_normal((B, Hkv, L, d))
+    v = rng.standard_normal((B, Hkv, L, d))
+    whole = oracle.attn_fwd(q, k, v, W)
+    kr = np.full((B, Hkv, W, d), np.nan)  # never-written slots stay NaN
+    vr = np.full((B, Hkv, W, d), np.nan)
+    p0 = 0
+    for T in chunks:
+        sl = slice(p0, p0 + T)
+        out = oracle.chunk_prefill(q[:, :, sl], k[:, :, sl], v[:, :, sl], kr, vr, [p0] * B, W)
+        assert np.abs(out - whole[:, :, sl]).max() <= 1e-12
+        kr, vr = oracle.ring_append(kr, vr, k[:, :, sl], v[:, :, sl], [p0] * B, W)
+        p0 += T
+    # and the cache then serves the decode step of the next token
+    qn = rng.standard_normal((B, Hq, d))
+    kn = rng.standard_normal((B, Hkv, 1, d))
+    vn = rng.standard_normal((B, Hkv, 1, d))
+    kr, vr = oracle.ring_append(kr, vr, kn, vn, [p0] * B, W)
+    dec = oracle.decode(qn, kr, vr, [p0 + 1] * B, W)
+    full = oracle.attn_fwd_rows(np.concatenate([q, qn[:, :, None]], 2), np.concatenate([k, kn], 2),
+                                np.concatenate([v, vn], 2), W, 0, 1 / math.sqrt(d),
+                                [(b, h, L) for b in range(B) for h in range(Hq)])
+    assert np.abs(dec.reshape(-1, d) - full).max() <= 1e-12
+
+
+def test_truncating_to_the_last_w_rows_is_not_the_rolling_cache():
+    """The SWA page §4.3 warns that cutting the input to its last W tokens and
+    recomputing is not the same as the rolling cache; in a single layer the
+    rows agree, so the difference shows in a second stacked layer, whose
+    inputs already mixed in older positions.  Here: one layer's rows are
+    identical either way (what the cache gives the next step)."""
+    W, L, d = 4, 10, 3
+    rng = np.random.default_rng(3)
+    q, k, v = (rng.standard_normal((1, 1, L, d)) for _ in range(3))
+    full_last = oracle.attn_fwd(q, k, v, W)[0, 0, -1]
+    cut_last = oracle.attn_fwd(q[:, :, -W:], k[:, :, -W:], v[:, :, -W:], W)[0, 0, -1]
+    assert np.abs(full_last - cut_last).max() <= 1e-12
+    # two stacked layers (output fed back as q, k and v): the cut input loses
+    # the older positions that the first layer had folded into rows L-W..L-1
+    h1 = oracle.attn_fwd(q, k, v, W)
+    two = oracle.attn_fwd(h1, h1, h1, W)[0, 0, -1]
+    h1c = oracle.attn_fwd(q[:, :, -W:], k[:, :, -W:], v[:, :, -W:], W)
+    two_cut = oracle.attn_fwd(h1c, h1c, h1c, W)[0, 0, -1]
+    assert np.abs(two - two_cut).max() > 1e-3
+
+
 # ---------------------------------------------------------------- pin strength
 def _pins_fail(monkeypatch, name, bad):
     """Run the pins with one oracle helper replaced; True if any pin fails."""
