@@ -13,6 +13,9 @@ counts against the kernel).  The same line carries:
                   profiles/ was taken on the current kernel source;
   * decode     -- the rolling-window decode step (64 sequences, W=4096 ring,
                   32/8 heads, d=128) in GB/s of algorithmic bytes vs 8 TB/s;
+  * chunk      -- chunked prefill over the rolling cache (4 sequences x 4096
+                  new tokens, cached lengths 0 / 1500 / 4095 / 61440) in
+                  in-band TFLOP/s, and the ring append of the same chunk;
   * cpu_baseline -- the float64 oracle on the host cores over a bounded
                   sample of the same workload (run before the GPU is touched,
                   since its worker pool forks).
@@ -137,6 +140,7 @@ def main():
     ap.add_argument("--workload", default="mistral", choices=["mistral", "gemma", "strided"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -231,6 +235,33 @@ def main():
                           "cpu_baseline": None if dec_cpu_s is None else
                           {"value": round(dbytes / dec_cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1,
                            "kind": "oracle", "sample": f"whole {dcfg.name} step, float64 numpy, {dec_cpu_s:.2f} s"}}
+
+    if not args.no_chunk:
+        ccfg = inputs.CHUNK
+        cq, ck, cv, ckr, cvr, cp0 = (x.to(dev) for x in inputs.chunk_inputs(ccfg))
+        cout = torch.empty_like(cq)
+
+        def cstep(i=0):
+            swa.chunk_prefill(cq, ck, cv, ckr, cvr, cp0, out=cout)
+
+        def astep(i=0):
+            # same slots every step (p0 fixed): the ring contents do not
+            # change the work of either kernel
+            swa.ring_append(ck, cv, cp0, ckr, cvr)
+
+        cper, _ = time_launches(cstep, args.steps, args.warmup, torch)
+        aper, _ = time_launches(astep, args.steps, args.warmup, torch)
+        cms, ams = sum(cper) / len(cper), sum(aper) / len(aper)
+        cpairs = sum(min(p + r + 1, ccfg.window) for p in ccfg.p0 for r in range(ccfg.T))
+        cflops = 4.0 * ccfg.Hq * ccfg.d * cpairs
+        abytes = 2 * 2 * len(ccfg.p0) * ccfg.Hkv * min(ccfg.T, ccfg.window) * ccfg.d * 2  # K,V read + write
+        line["chunk"] = {"workload": ccfg.name, "p0": list(ccfg.p0), "value": round(cflops / (cms * 1e-3) / 1e12, 2),
+                         "unit": "TFLOP/s", "frac_mfma": round(cflops / (cms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "avg_launch_ms": round(cms, 4), "algorithmic_flops_per_launch": cflops,
+                         "kernel": "band_fwd_kernel<bf16, d=128, chunk>",
+                         "ring_append": {"avg_launch_ms": round(ams, 4), "bytes": abytes,
+                                         "GB_s": round(abytes / (ams * 1e-3) / 1e9, 1)}}
+        del cq, ck, cv, ckr, cvr, cp0, cout
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

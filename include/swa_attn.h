@@ -113,6 +113,50 @@ SWA_API int swa_decode_f32(const float* q, const float* kring, const float* vrin
                    float* out, int B, int Hq, int Hkv, int d, float scale,
                    void* workspace, size_t workspace_bytes, int window, hipStream_t stream);
 
+/*
+ * Chunked prefill over the rolling cache (page "SWA：滑动窗口注意力与跨层信息传递",
+ * §4.3): a chunk of T new tokens attends to the cached history plus its own
+ * earlier rows, each row under its own band.  Chunk row r of sequence b is
+ * absolute position i = p0[b] + r + 1 and reads positions max(1, i-W+1) .. i:
+ * those up to p0[b] from the ring (position t in slot (t-1) % window), the
+ * rest from the chunk.  Call it BEFORE swa_ring_append writes the chunk into
+ * the ring: the append overwrites history that earlier rows of the chunk
+ * still read.
+ *   q, out       : [B, Hq, T, d]            k, v : [B, Hkv, T, d] (the chunk's K/V)
+ *   kring, vring : [B, Hkv, window, d] holding positions up to p0[b]
+ *   p0           : int32 [B] on the device, positions already cached (0 for
+ *                  the first chunk; values < 0 are read as 0).  Slots the step
+ *                  does not read may hold anything, NaN included.
+ *   T >= 1, window >= 1, d in {64, 128}, Hq % Hkv == 0; 16-byte aligned
+ *   pointers; scale finite and non-zero.  Same kernel as swa_attn_fwd (band
+ *   mode over the history followed by the chunk).
+ */
+SWA_API int swa_chunk_prefill(const void* q, const void* k, const void* v, const void* kring, const void* vring,
+                              const int32_t* p0, void* out, int B, int Hq, int Hkv, int T, int d, int window,
+                              float scale, hipStream_t stream);
+
+/* Same contract with fp32 tensors and fp32 matrix-core arithmetic. */
+SWA_API int swa_chunk_prefill_f32(const float* q, const float* k, const float* v, const float* kring,
+                                  const float* vring, const int32_t* p0, float* out, int B, int Hq, int Hkv, int T,
+                                  int d, int window, float scale, hipStream_t stream);
+
+/*
+ * Rolling-cache append (SWA page §4.2): chunk row r of sequence b (absolute
+ * position p0[b] + r + 1) is copied to slot (p0[b] + r) % window of kring and
+ * vring; of a chunk longer than the ring only the last `window` rows are
+ * written.  Bit-exact copy; afterwards the ring holds positions up to
+ * p0[b] + T, ready for the next chunk or for swa_decode with pos = p0[b] + T
+ * (+1 per later token).
+ *   k, v : [B, Hkv, T, d]   kring, vring : [B, Hkv, window, d]   p0 : int32 [B]
+ *   (device; < 0 read as 0).  16-byte aligned pointers, d in {64, 128}.
+ */
+SWA_API int swa_ring_append(const void* k, const void* v, const int32_t* p0, void* kring, void* vring, int B,
+                            int Hkv, int T, int d, int window, hipStream_t stream);
+
+/* Same for fp32 rings. */
+SWA_API int swa_ring_append_f32(const float* k, const float* v, const int32_t* p0, float* kring, float* vring,
+                                int B, int Hkv, int T, int d, int window, hipStream_t stream);
+
 /* Workspace bytes swa_decode / swa_decode_f32 need (0 when the split plan
    for these sizes has one split, and for invalid sizes). */
 SWA_API size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window);

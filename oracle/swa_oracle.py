@@ -314,9 +314,11 @@ def ring_append(kring, vring, k, v, p0, window: int):
     return kr, vr
 
 
-def chunk_prefill(q, k, v, kring, vring, p0, window: int, scale: Optional[float] = None) -> np.ndarray:
+def chunk_prefill(q, k, v, kring, vring, p0, window: int, scale: Optional[float] = None,
+                  rows=None) -> np.ndarray:
     """Attention of a chunk of T new tokens over the ring history plus the
-    chunk itself (SWA page §4.3), float64 [B, Hq, T, d].
+    chunk itself (SWA page §4.3), float64 [B, Hq, T, d] (or only the chunk
+    rows listed in ``rows``, ascending: [B, Hq, len(rows), d]).
 
     q: [B, Hq, T, d]; k, v: [B, Hkv, T, d] (the chunk's own keys/values);
     kring, vring: [B, Hkv, W, d] holding positions up to p0[b] (not yet the
@@ -333,7 +335,8 @@ def chunk_prefill(q, k, v, kring, vring, p0, window: int, scale: Optional[float]
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     G = Hq // k.shape[1]
-    out = np.empty((B, Hq, T, v.shape[3]), dtype=np.float64)
+    sel = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((B, Hq, len(sel), v.shape[3]), dtype=np.float64)
     for b in range(B):
         start = int(p0[b])
         n_hist = min(start, window - 1)  # older positions are outside every chunk row's window
@@ -346,6 +349,5 @@ def chunk_prefill(q, k, v, kring, vring, p0, window: int, scale: Optional[float]
             kk = np.concatenate([kring[b, g][slots], k[b, g]])
             vv = np.concatenate([vring[b, g][slots], v[b, g]])
             qq = np.concatenate([np.zeros((n_hist, d)), q[b, h]])
-            rows = np.arange(n_hist, n_hist + T, dtype=np.int64)
-            out[b, h] = _head_rows(qq, kk, vv, rows, window, 0, scale)
+            out[b, h] = _head_rows(qq, kk, vv, n_hist + sel, window, 0, scale)
     return out

@@ -10,7 +10,9 @@ from ._lib import (  # noqa: F401
     SIGNATURES,
     SwaError,
     attn_fwd,
+    chunk_prefill,
     decode,
     decode_workspace_bytes,
     lib,
+    ring_append,
 )

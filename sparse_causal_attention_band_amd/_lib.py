@@ -32,6 +32,10 @@ SIGNATURES = {
     "swa_attn_fwd_f32": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _Z, _I, _P]),
     "swa_decode_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _Z, _I, _P]),
+    "swa_chunk_prefill": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "swa_chunk_prefill_f32": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "swa_ring_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "swa_ring_append_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "swa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "swa_last_error": (ctypes.c_char_p, []),
 }
@@ -161,3 +165,63 @@ def decode(q: torch.Tensor, kring: torch.Tensor, vring: torch.Tensor, pos: torch
     _check(fn(q.data_ptr(), kring.data_ptr(), vring.data_ptr(), pos.data_ptr(), out.data_ptr(),
               B, Hq, kring.shape[1], d, float(scale), ws_ptr, ws_bytes, W, _stream(dev)))
     return out
+
+
+def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kring: torch.Tensor, vring: torch.Tensor,
+                  p0: torch.Tensor, scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """A chunk of new tokens over the rolling-cache history plus itself.
+
+    q: [B, Hq, T, d]; k, v: [B, Hkv, T, d]; kring, vring: [B, Hkv, W, d]
+    holding positions up to p0 (int32 [B] on the GPU).  Call before
+    ``ring_append`` of the same chunk.
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or kring.dim() != 4 or vring.shape != kring.shape:
+        raise ValueError("q, k, v must be [B, H, T, d] and kring, vring [B, Hkv, W, d]")
+    B, Hq, T, d = q.shape
+    if k.shape[0] != B or k.shape[2] != T or k.shape[3] != d:
+        raise ValueError("k, v do not match q")
+    if kring.shape[0] != B or kring.shape[1] != k.shape[1] or kring.shape[3] != d:
+        raise ValueError("rings do not match k, v")
+    dtype, dev = q.dtype, q.device
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bfloat16 or float32")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (kring, "kring"), (vring, "vring")):
+        _need(t, n, dtype, dev)
+    _need(p0, "p0", torch.int32, dev)
+    if p0.shape != (B,):
+        raise ValueError("p0 must be [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    fn = lib().swa_chunk_prefill if dtype == torch.bfloat16 else lib().swa_chunk_prefill_f32
+    _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), kring.data_ptr(), vring.data_ptr(), p0.data_ptr(),
+              out.data_ptr(), B, Hq, k.shape[1], T, d, kring.shape[2], float(scale), _stream(dev)))
+    return out
+
+
+def ring_append(k: torch.Tensor, v: torch.Tensor, p0: torch.Tensor, kring: torch.Tensor, vring: torch.Tensor):
+    """Write a chunk's K/V rows into the rolling cache in place (slot (p0+r) % W)."""
+    if k.dim() != 4 or v.shape != k.shape or kring.dim() != 4 or vring.shape != kring.shape:
+        raise ValueError("k, v must be [B, Hkv, T, d] and kring, vring [B, Hkv, W, d]")
+    B, Hkv, T, d = k.shape
+    if kring.shape[0] != B or kring.shape[1] != Hkv or kring.shape[3] != d:
+        raise ValueError("rings do not match k, v")
+    dtype, dev = k.dtype, k.device
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("k must be bfloat16 or float32")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    for t, n in ((k, "k"), (v, "v"), (kring, "kring"), (vring, "vring")):
+        _need(t, n, dtype, dev)
+    _need(p0, "p0", torch.int32, dev)
+    if p0.shape != (B,):
+        raise ValueError("p0 must be [B]")
+    fn = lib().swa_ring_append if dtype == torch.bfloat16 else lib().swa_ring_append_f32
+    _check(fn(k.data_ptr(), v.data_ptr(), p0.data_ptr(), kring.data_ptr(), vring.data_ptr(), B, Hkv, T, d,
+              kring.shape[2], _stream(dev)))

@@ -13,7 +13,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["swa_api.hip", "swa_band_fwd.hip", "swa_decode.hip"]
+SOURCES = ["swa_api.hip", "swa_band_fwd.hip", "swa_decode.hip", "swa_ring.hip"]
 LIB_NAME = "libswa_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")

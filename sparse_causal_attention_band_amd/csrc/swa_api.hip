@@ -71,6 +71,9 @@ int attn_fwd(bool bf16, const void* q, const void* k, const void* v, void* out, 
     p.k = k;
     p.v = v;
     p.out = out;
+    p.kring = nullptr;
+    p.vring = nullptr;
+    p.p0 = nullptr;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
@@ -88,7 +91,71 @@ int attn_fwd(bool bf16, const void* q, const void* k, const void* v, void* out, 
     const long long total = (long long)B * Hkv * p.ngroups * p.nqb;
     if (total > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
     p.total = (int)total;
-    hipError_t e = swa::launch_band_fwd(bf16, d, p.stride > 0, p, stream);
+    hipError_t e = swa::launch_band_fwd(bf16, d, p.stride > 0 ? swa::kStrided : swa::kBand, p, stream);
+    if (e != hipSuccess) return fail(SWA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
+    return ok();
+}
+
+int chunk_prefill(bool bf16, const void* q, const void* k, const void* v, const void* kring, const void* vring,
+                  const int32_t* p0, void* out, int B, int Hq, int Hkv, int T, int d, int window, float scale,
+                  hipStream_t stream) {
+    const char* name = bf16 ? "swa_chunk_prefill" : "swa_chunk_prefill_f32";
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1)
+        return fail(SWA_ERR_INVALID_ARG, "%s: B, T, Hq, Hkv must be >= 1 (B=%d T=%d Hq=%d Hkv=%d)", name, B, T, Hq,
+                    Hkv);
+    if (Hq % Hkv != 0) return fail(SWA_ERR_INVALID_ARG, "%s: Hq (%d) must be a multiple of Hkv (%d)", name, Hq, Hkv);
+    if (window < 1) return fail(SWA_ERR_INVALID_ARG, "%s: window must be >= 1 (got %d)", name, window);
+    if (d != 64 && d != 128) return fail(SWA_ERR_UNSUPPORTED, "%s: head dim %d not built (64 or 128)", name, d);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(kring) || !aligned16(vring))
+        return fail(SWA_ERR_INVALID_ARG, "%s: q, k, v, kring, vring, out must be non-null and 16-byte aligned", name);
+    if (p0 == nullptr || ((uintptr_t)p0 & 3u))
+        return fail(SWA_ERR_INVALID_ARG, "%s: p0 must be non-null, 4-byte aligned", name);
+    if (int rc = check_scale(name, scale)) return rc;
+    if ((long long)T + window > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: T + window too large", name);
+    const long long G = Hq / Hkv;
+    swa::PrefillParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.kring = kring;
+    p.vring = vring;
+    p.p0 = p0;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.N = T;
+    p.W = window;  // the ring size; the kernel clamps the band to the keys it has
+    p.stride = 0;
+    p.c = fabsf(scale) * kLog2e;
+    p.neg = scale < 0.f;
+    p.G = (int)G;
+    p.HG = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+    p.PB = 4 / p.HG;
+    const int BM = swa::kQueriesPerWave * p.PB;
+    p.nqb = (T + BM - 1) / BM;
+    p.ngroups = (int)G / p.HG;
+    const long long total = (long long)B * Hkv * p.ngroups * p.nqb;
+    if (total > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
+    p.total = (int)total;
+    hipError_t e = swa::launch_band_fwd(bf16, d, swa::kChunk, p, stream);
+    if (e != hipSuccess) return fail(SWA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
+    return ok();
+}
+
+int ring_append(bool bf16, const void* k, const void* v, const int32_t* p0, void* kring, void* vring, int B, int Hkv,
+                int T, int d, int window, hipStream_t stream) {
+    const char* name = bf16 ? "swa_ring_append" : "swa_ring_append_f32";
+    if (B < 1 || T < 1 || Hkv < 1 || window < 1)
+        return fail(SWA_ERR_INVALID_ARG, "%s: B, T, Hkv, window must be >= 1 (B=%d T=%d Hkv=%d window=%d)", name, B,
+                    T, Hkv, window);
+    if (d != 64 && d != 128) return fail(SWA_ERR_UNSUPPORTED, "%s: head dim %d not built (64 or 128)", name, d);
+    if (!aligned16(k) || !aligned16(v) || !aligned16(kring) || !aligned16(vring))
+        return fail(SWA_ERR_INVALID_ARG, "%s: k, v, kring, vring must be non-null and 16-byte aligned", name);
+    if (p0 == nullptr || ((uintptr_t)p0 & 3u))
+        return fail(SWA_ERR_INVALID_ARG, "%s: p0 must be non-null, 4-byte aligned", name);
+    if (B > 65535 || Hkv > 65535) return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
+    hipError_t e = swa::launch_ring_append(bf16 ? 2 : 4, d, k, v, p0, kring, vring, B, Hkv, T, window, stream);
     if (e != hipSuccess) return fail(SWA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
     return ok();
 }
@@ -162,6 +229,28 @@ int swa_decode_f32(const float* q, const float* kring, const float* vring, const
                    int Hq, int Hkv, int d, float scale, void* workspace, size_t workspace_bytes, int window,
                    hipStream_t stream) {
     return decode(false, q, kring, vring, pos, out, B, Hq, Hkv, d, scale, workspace, workspace_bytes, window, stream);
+}
+
+int swa_chunk_prefill(const void* q, const void* k, const void* v, const void* kring, const void* vring,
+                      const int32_t* p0, void* out, int B, int Hq, int Hkv, int T, int d, int window, float scale,
+                      hipStream_t stream) {
+    return chunk_prefill(true, q, k, v, kring, vring, p0, out, B, Hq, Hkv, T, d, window, scale, stream);
+}
+
+int swa_chunk_prefill_f32(const float* q, const float* k, const float* v, const float* kring, const float* vring,
+                          const int32_t* p0, float* out, int B, int Hq, int Hkv, int T, int d, int window,
+                          float scale, hipStream_t stream) {
+    return chunk_prefill(false, q, k, v, kring, vring, p0, out, B, Hq, Hkv, T, d, window, scale, stream);
+}
+
+int swa_ring_append(const void* k, const void* v, const int32_t* p0, void* kring, void* vring, int B, int Hkv, int T,
+                    int d, int window, hipStream_t stream) {
+    return ring_append(true, k, v, p0, kring, vring, B, Hkv, T, d, window, stream);
+}
+
+int swa_ring_append_f32(const float* k, const float* v, const int32_t* p0, float* kring, float* vring, int B, int Hkv,
+                        int T, int d, int window, hipStream_t stream) {
+    return ring_append(false, k, v, p0, kring, vring, B, Hkv, T, d, window, stream);
 }
 
 size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window) {

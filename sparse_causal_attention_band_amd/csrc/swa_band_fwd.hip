@@ -2,6 +2,8 @@
 //
 // What it computes: softmax(scale * Q K^T + M) V row by row, where row i may
 // read key j iff j <= i and (i - j < W or (stride > 0 and j % stride == 0)).
+// A third mode runs the same band over a chunk of new queries whose keys are
+// the rolling-cache history followed by the chunk itself (chunked prefill).
 // The band is the set N_W(i) of the page "SWA：滑动窗口注意力与跨层信息传递"
 // (§3.1, window counting the current position), the strided keys are the
 // "local + strided" mask of the page "注意力变体——滑动窗口、稀疏、差分"
@@ -99,8 +101,12 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
         (__attribute__((address_space(3))) i16x4_t*)(p));
 }
 
-template <bool BF, int D, bool STRIDED>
+// MODE: kBand (window only), kStrided (window + multiples of the stride),
+// kChunk (a chunk of new queries over the ring history plus the chunk).
+template <bool BF, int D, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) {
+    constexpr bool STRIDED = MODE == kStrided;
+    constexpr bool CHUNK = MODE == kChunk;
     using elem_t = typename std::conditional<BF, uint16_t, float>::type;
     using frag_t = typename std::conditional<BF, bf16x8_t, float>::type;
     constexpr int RB = D * (int)sizeof(elem_t);      // bytes per K/V row
@@ -137,12 +143,28 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     rest /= p.ngroups;
     const int kvh = rest % p.Hkv;
     const int b = rest / p.Hkv;
-    const int N = p.N, W = p.W;
+    const int N = p.N;
+    // Chunk mode (SWA page §4.3): the N queries are chunk rows that follow
+    // `start` cached positions.  They are placed at the end of a virtual
+    // sequence of NK = qoff + N keys whose first qoff = min(start, W-1) keys
+    // are the history read from the ring (older positions are outside every
+    // row's window) and whose last N keys are the chunk's own rows.  In the
+    // other modes qoff = 0 and the virtual sequence is the input.
+    int qoff = 0, hslot0 = 0;
+    if constexpr (CHUNK) {
+        const int start = max(p.p0[b], 0);
+        qoff = min(start, p.W - 1);
+        hslot0 = (start - qoff) % p.W;  // ring slot of the oldest history position used
+    }
+    const int NK = qoff + N;
+    const int W = min(p.W, NK);  // a wider window reads the same keys
     const int BM = kQw * p.PB;
     const int q0 = qb * BM;
     const int h = kvh * p.G + hg * p.HG + (wave % p.HG);
     const int qw0 = q0 + kQw * (wave / p.HG);
-    const int qi = qw0 + l32;
+    const int qi = qw0 + l32;        // query row in q / out
+    const int qv = qoff + qi;        // its position in the virtual sequence
+    const int qvw0 = qoff + qw0;
 
     const size_t kv_head = (size_t)(b * p.Hkv + kvh) * (size_t)N * D;
     const size_t q_head = (size_t)(b * p.Hq + h) * (size_t)N * D;
@@ -150,11 +172,14 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     const elem_t* vg = (const elem_t*)p.v + kv_head;
     const elem_t* qg = (const elem_t*)p.q + q_head;
     elem_t* og = (elem_t*)p.out + q_head;
+    const size_t ring_head = (size_t)(b * p.Hkv + kvh) * (size_t)p.W * D;
+    const elem_t* krg = CHUNK ? (const elem_t*)p.kring + ring_head : nullptr;
+    const elem_t* vrg = CHUNK ? (const elem_t*)p.vring + ring_head : nullptr;
 
     // ---- key tiles of this workgroup: band tiles kt_hi .. kt_lo, then the
     // compact strided tiles (keys m*stride < kt_lo*64, read by every row).
-    const int kt_hi = min(N - 1, q0 + BM - 1) / kTileN;
-    const int kt_lo = max(0, q0 - W + 1) / kTileN;
+    const int kt_hi = min(NK - 1, qoff + q0 + BM - 1) / kTileN;
+    const int kt_lo = max(0, qoff + q0 - W + 1) / kTileN;
     const int nband = kt_hi - kt_lo + 1;
     int M = 0, ncomp = 0;
     if (STRIDED) {
@@ -202,10 +227,23 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     // which global 16-byte chunk each lane fetches.  Rows past the end are clamped to a valid row: those keys are
     // always masked, and the copy never leaves non-finite bits in LDS.
     auto issue_tile = [&](int t, char* kl, char* vl, bool do_k, bool do_v) __attribute__((always_inline)) {
-        // key row behind tile row r
+        // key row behind tile row r (virtual index in chunk mode)
         auto key_of = [&](int r) __attribute__((always_inline)) {
-            return t < nband ? min((kt_hi - t) * kTileN + r, N - 1)
+            return t < nband ? min((kt_hi - t) * kTileN + r, NK - 1)
                              : min((t - nband) * kTileN + r, M - 1) * p.stride;
+        };
+        // its row in HBM: the input, or in chunk mode the ring for history keys
+        auto row_ptr = [&](const elem_t* in, const elem_t* ring, int j) __attribute__((always_inline)) {
+            if constexpr (CHUNK) {
+                if (j < qoff) {
+                    int slot = hslot0 + j;
+                    slot -= slot >= p.W ? p.W : 0;
+                    return ring + (size_t)slot * D;
+                }
+                return in + (size_t)(j - qoff) * D;
+            } else {
+                return in + (size_t)j * D;
+            }
         };
 #pragma unroll
         for (int it = 0; it < NCH; ++it) {
@@ -215,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
             const int within = P % (CPR * 256);
             const int pos = (P / (CPR * 256)) * 16 + ((within >> 4) & 15);
             const int ch = within >> 8;
-            const char* src = (const char*)(kg + (size_t)key_of(sigma(pos)) * D) + (ch << 4);
+            const char* src = (const char*)row_ptr(kg, krg, key_of(sigma(pos))) + (ch << 4);
             __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(kl + blk), 16, 0, 0);
         }
 #pragma unroll
@@ -225,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
             const int P = blk + lane * 16;
             const int row = P / RBV, inrow = P % RBV;
             if (inrow < RB) {
-                const char* src = (const char*)(vg + (size_t)key_of(row) * D) + inrow;
+                const char* src = (const char*)row_ptr(vg, vrg, key_of(row)) + inrow;
                 __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(vl + blk), 16, 0, 0);
             }
         }
@@ -264,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     auto mask_tile = [&](int t, f32x16_t* sc) __attribute__((always_inline)) {
         const bool band = t < nband;
         const int j0 = (kt_hi - t) * kTileN;
-        const bool edge = band ? !(j0 + kTileN - 1 <= qw0 && j0 >= qw0 + kQw - W)
+        const bool edge = band ? !(j0 + kTileN - 1 <= qvw0 && j0 >= qvw0 + kQw - W)
                                : ((t - nband + 1) * kTileN > M);
         if (edge) {
             // bit o of smask: key j0 + o is a multiple of the stride
@@ -280,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
                     // non-short-circuit operators: a straight-line select,
                     // no per-element divergent branches
                     const int r = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
-                    const int dist = qi - (j0 + r);
+                    const int dist = qv - (j0 + r);
                     const bool in_band = (dist >= 0) & ((dist < W) | (STRIDED & (((smask >> r) & 1ull) != 0)));
                     const bool in_comp = (t - nband) * kTileN + r < M;
                     sc[kb][i] = (band ? in_band : in_comp) ? sc[kb][i] : -INFINITY;
@@ -436,21 +474,24 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
         }
 }
 
-template <bool BF, int D, bool STRIDED>
+template <bool BF, int D, int MODE>
 hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((band_fwd_kernel<BF, D, STRIDED>), dim3(p.total), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((band_fwd_kernel<BF, D, MODE>), dim3(p.total), dim3(kThreads), 0, s, p);
     return hipGetLastError();
+}
+
+template <bool BF, int D>
+hipError_t launch_mode(int mode, const PrefillParams& p, hipStream_t s) {
+    if (mode == kStrided) return launch_one<BF, D, kStrided>(p, s);
+    if (mode == kChunk) return launch_one<BF, D, kChunk>(p, s);
+    return launch_one<BF, D, kBand>(p, s);
 }
 
 }  // namespace
 
-hipError_t launch_band_fwd(bool bf16, int d, bool strided, const PrefillParams& p, hipStream_t s) {
-    if (bf16) {
-        if (d == 128) return strided ? launch_one<true, 128, true>(p, s) : launch_one<true, 128, false>(p, s);
-        return strided ? launch_one<true, 64, true>(p, s) : launch_one<true, 64, false>(p, s);
-    }
-    if (d == 128) return strided ? launch_one<false, 128, true>(p, s) : launch_one<false, 128, false>(p, s);
-    return strided ? launch_one<false, 64, true>(p, s) : launch_one<false, 64, false>(p, s);
+hipError_t launch_band_fwd(bool bf16, int d, int mode, const PrefillParams& p, hipStream_t s) {
+    if (bf16) return d == 128 ? launch_mode<true, 128>(mode, p, s) : launch_mode<true, 64>(mode, p, s);
+    return d == 128 ? launch_mode<false, 128>(mode, p, s) : launch_mode<false, 64>(mode, p, s);
 }
 
 }  // namespace swa

@@ -9,13 +9,18 @@
 namespace swa {
 
 // ---------------------------------------------------------------- prefill
+enum { kBand = 0, kStrided = 1, kChunk = 2 };
+
 struct PrefillParams {
     const void* q;
     const void* k;
     const void* v;
     void* out;
+    const void* kring;     // chunk mode: [B, Hkv, W, d] history ring
+    const void* vring;
+    const int32_t* p0;     // chunk mode: [B] positions already cached
     int B, Hq, Hkv, N;
-    int W;        // window, already clamped to N
+    int W;        // window (band modes: clamped to N; chunk mode: the ring size)
     int stride;   // > 0 only for the strided instantiation
     float c;      // |scale| * log2(e): scores are kept in the log2 domain
     int neg;      // scale < 0: queries enter with flipped sign (exact)
@@ -27,8 +32,12 @@ struct PrefillParams {
     int total;    // workgroups in the grid
 };
 
-// Launch the band kernel for one (dtype, head dim, strided) combination.
-hipError_t launch_band_fwd(bool bf16, int d, bool strided, const PrefillParams& p, hipStream_t s);
+// Launch the band kernel for one (dtype, head dim, mode) combination.
+hipError_t launch_band_fwd(bool bf16, int d, int mode, const PrefillParams& p, hipStream_t s);
+
+// Copy a chunk's K/V rows into their ring slots (position t -> slot (t-1) % W).
+hipError_t launch_ring_append(int elem_bytes, int d, const void* k, const void* v, const int32_t* p0, void* kring,
+                              void* vring, int B, int Hkv, int T, int W, hipStream_t s);
 
 // Rows of one workgroup tile, for host-side bookkeeping and tests.
 constexpr int kQueriesPerWave = 32;

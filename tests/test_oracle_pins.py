@@ -320,6 +320,8 @@ def test_chunked_prefill_equals_whole_prefill(W, chunks):
         sl = slice(p0, p0 + T)
         out = oracle.chunk_prefill(q[:, :, sl], k[:, :, sl], v[:, :, sl], kr, vr, [p0] * B, W)
         assert np.abs(out - whole[:, :, sl]).max() <= 1e-12
+        last = oracle.chunk_prefill(q[:, :, sl], k[:, :, sl], v[:, :, sl], kr, vr, [p0] * B, W, rows=[T - 1])
+        assert np.abs(last[:, :, 0] - whole[:, :, p0 + T - 1]).max() <= 1e-12
         kr, vr = oracle.ring_append(kr, vr, k[:, :, sl], v[:, :, sl], [p0] * B, W)
         p0 += T
     # and the cache then serves the decode step of the next token
