@@ -83,11 +83,7 @@ int attn_fwd(bool bf16, const void* q, const void* k, const void* v, void* out, 
     p.c = fabsf(scale) * kLog2e;
     p.neg = scale < 0.f;
     p.G = (int)G;
-    p.HG = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-    p.PB = 4 / p.HG;
-    const int BM = swa::kQueriesPerWave * p.PB;
-    p.nqb = (N + BM - 1) / BM;
-    p.ngroups = (int)G / p.HG;
+    swa::set_wave_split(p, swa::waves_per_group(bf16, p.stride > 0, p.G), N);
     const long long total = (long long)B * Hkv * p.ngroups * p.nqb;
     if (total > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
     p.total = (int)total;
@@ -130,11 +126,7 @@ int chunk_prefill(bool bf16, const void* q, const void* k, const void* v, const 
     p.c = fabsf(scale) * kLog2e;
     p.neg = scale < 0.f;
     p.G = (int)G;
-    p.HG = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-    p.PB = 4 / p.HG;
-    const int BM = swa::kQueriesPerWave * p.PB;
-    p.nqb = (T + BM - 1) / BM;
-    p.ngroups = (int)G / p.HG;
+    swa::set_wave_split(p, swa::waves_per_group(bf16, false, p.G), T);
     const long long total = (long long)B * Hkv * p.ngroups * p.nqb;
     if (total > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
     p.total = (int)total;

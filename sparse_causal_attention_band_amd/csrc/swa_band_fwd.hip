@@ -12,7 +12,12 @@
 // page, 稀疏 / 块注意力: never bring the zero entries on chip), so the kernel
 // enumerates only key tiles that meet the band.
 //
-// Structure (one workgroup = 4 waves = 256 threads):
+// Two kernels share the tile enumeration, layouts, masking and softmax: the
+// 8-wave bf16 kernel at the end of this file (band and chunk modes with at
+// least four query heads per KV head) and the 4-wave kernel described here
+// (fp32, the strided mode, and fewer grouped heads).
+//
+// Structure of the 4-wave kernel (one workgroup = 4 waves = 256 threads):
 //  * A workgroup owns 4 blocks of 32 queries: HG query heads that share one
 //    KV head times PB position blocks (HG * PB = 4).  Grouped heads therefore
 //    read every K/V tile from LDS once per workgroup.
@@ -474,8 +479,397 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
         }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel: 8 waves per workgroup sharing one K/V tile stream, with three
+// K and three V buffers so that every copy is issued two tiles before it is
+// read.  The tile list, the K layout, masking and the online softmax are
+// those of the 4-wave kernel above; the differences are:
+//  * V is stored unpadded with its 64-byte quarters XOR-swizzled by row, so
+//    that the four rows an 8-byte transpose read touches in one cycle fall
+//    on four different bank quarters; a tile is then 8 KiB-aligned and every
+//    wave copies the same number of 1 KiB blocks;
+//  * step t reads K(t+1) (next scores) and V(t) (this tile's P*V), issues
+//    K(t+3) and V(t+2), and waits only for the copies issued one step earlier;
+//  * this tile's probabilities, its P*V product and the next tile's scores
+//    form one straight-line block, 16 keys at a time, so that every matrix
+//    instruction has vector work of the same wave beside it.
+constexpr int kThreads8 = 512;
+
+__device__ __forceinline__ void lds_barrier() {
+    // this wave's LDS reads done, then the workgroup barrier: no fence, so
+    // the copies in flight are not drained
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(PrefillParams p) {
+    constexpr bool STRIDED = MODE == kStrided;
+    constexpr bool CHUNK = MODE == kChunk;
+    using elem_t = uint16_t;
+    constexpr int RB = D * 2;                    // bytes per K/V row
+    constexpr int CPR = RB / 16;                 // 16-byte chunks per row
+    constexpr int TILE_BYTES = kTileN * RB;      // K or V tile
+    constexpr int NBLK = TILE_BYTES / 8192;      // 1 KiB copy blocks per wave per tile
+    constexpr int NDB = D / 32;                  // 32-row blocks of O^T
+    constexpr int NQF = D / 16;                  // Q fragments
+    static_assert(TILE_BYTES % 8192 == 0, "copy split");
+    static_assert(NDB == NQF / 2, "one P*V instruction per score instruction");
+
+    __shared__ __attribute__((aligned(16))) char kb0[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char kb1[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char kb2[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char vb0[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char vb1[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char vb2[TILE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS copy targets stay scalar
+    const int g = lane >> 5, l32 = lane & 31;
+
+    const int L = xcd_remap(blockIdx.x, p.total);
+    const int qb = L % p.nqb;
+    int rest = L / p.nqb;
+    const int hg = rest % p.ngroups;
+    rest /= p.ngroups;
+    const int kvh = rest % p.Hkv;
+    const int b = rest / p.Hkv;
+    const int N = p.N;
+    int qoff = 0, hslot0 = 0;
+    if constexpr (CHUNK) {
+        const int start = max(p.p0[b], 0);
+        qoff = min(start, p.W - 1);
+        hslot0 = (start - qoff) % p.W;
+    }
+    const int NK = qoff + N;
+    const int W = min(p.W, NK);
+    const int BM = kQw * p.PB;
+    const int q0 = qb * BM;
+    const int h = kvh * p.G + hg * p.HG + (wave % p.HG);
+    const int qw0 = q0 + kQw * (wave / p.HG);
+    const int qi = qw0 + l32;
+    const int qv = qoff + qi;
+    const int qvw0 = qoff + qw0;
+
+    const size_t kv_head = (size_t)(b * p.Hkv + kvh) * (size_t)N * D;
+    const size_t q_head = (size_t)(b * p.Hq + h) * (size_t)N * D;
+    const elem_t* kg = (const elem_t*)p.k + kv_head;
+    const elem_t* vg = (const elem_t*)p.v + kv_head;
+    const elem_t* qg = (const elem_t*)p.q + q_head;
+    elem_t* og = (elem_t*)p.out + q_head;
+    const size_t ring_head = (size_t)(b * p.Hkv + kvh) * (size_t)p.W * D;
+    const elem_t* krg = CHUNK ? (const elem_t*)p.kring + ring_head : nullptr;
+    const elem_t* vrg = CHUNK ? (const elem_t*)p.vring + ring_head : nullptr;
+
+    const int kt_hi = min(NK - 1, qoff + q0 + BM - 1) / kTileN;
+    const int kt_lo = max(0, qoff + q0 - W + 1) / kTileN;
+    const int nband = kt_hi - kt_lo + 1;
+    int M = 0, ncomp = 0;
+    if (STRIDED) {
+        M = (kt_lo * kTileN + p.stride - 1) / p.stride;
+        ncomp = (M + kTileN - 1) / kTileN;
+    }
+    const int ntiles = nband + ncomp;
+    const bool wave_live = qw0 < N;
+
+    bf16x8_t qf[NQF];
+    {
+        const uint32_t flip = p.neg ? 0x80008000u : 0u;
+        const uint32_t keep = qi < N ? 0xffffffffu : 0u;
+        const size_t qrow = (size_t)min(qi, N - 1) * D;
+#pragma unroll
+        for (int c = 0; c < NQF; ++c) {
+            u32x4_t w = *(const u32x4_t*)(qg + qrow + 16 * c + 8 * g);
+            w = (w & keep) ^ flip;
+            qf[c] = __builtin_bit_cast(bf16x8_t, w);
+        }
+    }
+
+    // V swizzle: the 64-byte quarter q of row r is stored at quarter
+    // q ^ vswz(r) (d=128: r mod 4; d=64: bit 1 of r)
+    auto vswz = [](int r) __attribute__((always_inline)) {
+        return D == 128 ? ((r & 3) << 6) : (((r >> 1) & 1) << 6);
+    };
+    const int k_lane = (((l32 >> 4) * CPR + g) << 8) + ((l32 & 15) << 4);
+    // V transpose read: row 8*g + (lane&15)/4 (+16*c2, +4), bytes
+    // 32*((lane>>4)&1) + 8*(lane&3) of quarter db (swizzled)
+    const int v_row = 8 * g + ((lane & 15) >> 2);
+    const int v_lane = v_row * RB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+    const int vq = vswz(v_row);
+
+    auto key_of = [&](int t, int r) __attribute__((always_inline)) {
+        return t < nband ? min((kt_hi - t) * kTileN + r, NK - 1) : min((t - nband) * kTileN + r, M - 1) * p.stride;
+    };
+    auto row_ptr = [&](const elem_t* in, const elem_t* ring, int j) __attribute__((always_inline)) {
+        if constexpr (CHUNK) {
+            if (j < qoff) {
+                int slot = hslot0 + j;
+                slot -= slot >= p.W ? p.W : 0;
+                return ring + (size_t)slot * D;
+            }
+            return in + (size_t)(j - qoff) * D;
+        } else {
+            return in + (size_t)j * D;
+        }
+    };
+    // copies: wave w fills 1 KiB blocks w, w+8, ... of the tile (lane i
+    // writes bytes 16i..16i+15 of a block).  Per block the lane's source is
+    // a fixed byte offset inside the tile's 64 rows (K: row sigma(pos),
+    // chunk ch; V: the swizzled quarter), so a tile whose rows are 64
+    // consecutive rows of one array costs one scalar base per tile.  Other
+    // tiles (the clamped diagonal tile, strided rows, a ring wrap or the
+    // ring/chunk seam) take the general per-row path.
+    uint32_t koff[NBLK], voff[NBLK];  // row * RB + byte in row; row = off / RB
+#pragma unroll
+    for (int it = 0; it < NBLK; ++it) {
+        const int P = (wave + 8 * it) * 1024 + lane * 16;
+        const int within = P % (CPR * 256);
+        const int pos = (P / (CPR * 256)) * 16 + ((within >> 4) & 15);
+        koff[it] = (uint32_t)(sigma(pos) * RB + ((within >> 8) << 4));
+        const int vr = P / RB;
+        voff[it] = (uint32_t)(vr * RB + ((P % RB) ^ vswz(vr)));
+    }
+    // first row of tile t in the virtual sequence, and whether its 64 rows
+    // are consecutive rows of one array (the returned base)
+    auto tile_base = [&](int t, const elem_t* in, const elem_t* ring, const char*& base) __attribute__((always_inline)) {
+        if (t >= nband) return false;
+        const int j0 = (kt_hi - t) * kTileN;
+        if (j0 + kTileN > NK) return false;
+        if constexpr (CHUNK) {
+            if (j0 >= qoff) {
+                base = (const char*)(in + (size_t)(j0 - qoff) * D);
+                return true;
+            }
+            if (j0 + kTileN <= qoff && hslot0 + j0 + kTileN <= p.W) {
+                base = (const char*)(ring + (size_t)(hslot0 + j0) * D);
+                return true;
+            }
+            return false;
+        } else {
+            base = (const char*)(in + (size_t)j0 * D);
+            return true;
+        }
+    };
+    // The empty asm statements in the two paths differ, which keeps the
+    // compiler from merging their last loads into one flat-address load.
+    auto issue_rows = [&](int t, char* dst, const elem_t* in, const elem_t* ring, const uint32_t* off)
+        __attribute__((always_inline)) {
+        const char* base;
+        if (!STRIDED && tile_base(t, in, ring, base)) {
+#pragma unroll
+            for (int it = 0; it < NBLK; ++it)
+                __builtin_amdgcn_global_load_lds(base + off[it],
+                                                 (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024),
+                                                 16, 0, 0);
+            asm volatile("; tile copy: contiguous rows" ::: "memory");
+        } else {
+#pragma unroll
+            for (int it = 0; it < NBLK; ++it) {
+                const int row = (int)(off[it] / RB);
+                const char* src = (const char*)row_ptr(in, ring, key_of(t, row)) + (off[it] % RB);
+                __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024),
+                                                 16, 0, 0);
+            }
+            asm volatile("; tile copy: gathered rows" ::: "memory");
+        }
+    };
+    auto issue_k = [&](int t, char* kl) __attribute__((always_inline)) { issue_rows(t, kl, kg, krg, koff); };
+    auto issue_v = [&](int t, char* vl) __attribute__((always_inline)) { issue_rows(t, vl, vg, vrg, voff); };
+    // Every step issues the same copies (past the end of the list the last
+    // tile again, into a buffer nobody reads any more), so one fixed wait
+    // count holds: the 2*NBLK loads of the current step may stay in flight.
+    auto wait_older_copies = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0xF70 | (2 * NBLK)); };
+
+    f32x16_t oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    const float c = p.c;
+    float alpha = 1.f;
+
+    auto scores = [&](const char* kl, f32x16_t* sc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < NQF; ++cc) {
+                const bf16x8_t a = *(const bf16x8_t*)(kl + k_lane + ((kb * 2 * CPR + 2 * cc) << 8));
+                sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], sc[kb], 0, 0, 0);
+            }
+        }
+    };
+    auto mask_tile = [&](int t, f32x16_t* sc) __attribute__((always_inline)) {
+        const bool band = t < nband;
+        const int j0 = (kt_hi - t) * kTileN;
+        const bool edge = band ? !(j0 + kTileN - 1 <= qvw0 && j0 >= qvw0 + kQw - W) : ((t - nband + 1) * kTileN > M);
+        if (edge) {
+            uint64_t smask = 0;
+            if (STRIDED && band) {
+                const int r0 = j0 % p.stride;
+                for (int o = r0 == 0 ? 0 : p.stride - r0; o < kTileN; o += p.stride) smask |= 1ull << o;
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
+                    const int dist = qv - (j0 + r);
+                    const bool in_band = (dist >= 0) & ((dist < W) | (STRIDED & (((smask >> r) & 1ull) != 0)));
+                    const bool in_comp = (t - nband) * kTileN + r < M;
+                    sc[kb][i] = (band ? in_band : in_comp) ? sc[kb][i] : -INFINITY;
+                }
+        }
+    };
+    auto softmax_head = [&](f32x16_t* sc) __attribute__((always_inline)) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
+        mx = partner_max(mx);
+        const float m_cand = fmaxf(m_run, mx * c);
+        const bool grow = m_cand > m_run + 8.f;
+        alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_cand) : 1.f;
+        m_run = grow ? m_cand : m_run;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        }
+    };
+    // Tile work of one step, in one straight-line block: DO_PV = this tile's
+    // probabilities, row sum and P*V (from sc, vl); DO_S = the next tile's
+    // scores (into sn, from kl).  16 keys at a time, so that every matrix
+    // instruction has vector work of the same wave beside it.
+    auto tile_work = [&](auto do_pv, auto do_s, f32x16_t* sc, f32x16_t* sn, const char* kl, const char* vl)
+        __attribute__((always_inline)) {
+        constexpr bool DP = decltype(do_pv)::value, DS = decltype(do_s)::value;
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float rsv[4];
+        bf16x8_t pb[4];
+        if constexpr (DS) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sn[kb][i] = 0.f;
+        }
+        auto probs = [&](int c2) __attribute__((always_inline)) {
+            u32x4_t pw;
+            rsv[c2] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x0 = __builtin_amdgcn_exp2f(fmaf(sc[c2 >> 1][8 * (c2 & 1) + 2 * e], c, -m_use));
+                const float x1 = __builtin_amdgcn_exp2f(fmaf(sc[c2 >> 1][8 * (c2 & 1) + 2 * e + 1], c, -m_use));
+                const bf16x2_t pr = {(__bf16)x0, (__bf16)x1};
+                rsv[c2] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rsv[c2], false);
+                pw[e] = __builtin_bit_cast(uint32_t, pr);
+            }
+            pb[c2] = __builtin_bit_cast(bf16x8_t, pw);
+            asm volatile("" : "+v"(rsv[c2]));  // keep the dot chain beside its exponentials
+        };
+        auto mfmas = [&](int c2) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < NQF / 2; ++i) {
+                if constexpr (DS) {
+                    const int kb = i & 1, cc = c2 * (NQF / 4) + (i >> 1);
+                    const bf16x8_t a = *(const bf16x8_t*)(kl + k_lane + ((kb * 2 * CPR + 2 * cc) << 8));
+                    sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], sn[kb], 0, 0, 0);
+                }
+                if constexpr (DP) {
+                    const int db = i;
+                    const char* vp = vl + v_lane + ((64 * db) ^ vq) + 16 * c2 * RB;
+                    const i16x4_t lo = lds_read_tr16(vp);
+                    const i16x4_t hi = lds_read_tr16(vp + 4 * RB);
+                    const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
+                    const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
+                    const u32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a4), pb[c2],
+                                                                      oacc[db], 0, 0, 0);
+                }
+            }
+        };
+        if constexpr (DP) probs(0);
+#pragma unroll
+        for (int c2 = 0; c2 < 4; ++c2) {
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(c2);
+            if constexpr (DP) {
+                if (c2 < 3) probs(c2 + 1);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (DP) l_run = l_run * alpha + ((rsv[0] + rsv[1]) + (rsv[2] + rsv[3]));
+    };
+
+    const int n = ntiles;
+    // prologue: K(0), scores of tile 0; then K(1), V(0), K(2), V(1) in flight
+    issue_k(0, kb0);
+    __builtin_amdgcn_s_waitcnt(0xF70);
+    lds_barrier();
+    f32x16_t scur[2];
+    scores(kb0, scur);
+    mask_tile(0, scur);
+    lds_barrier();  // tile 0's K reads are done before K(3) lands in kb0
+    issue_k(min(1, n - 1), kb1);
+    issue_v(0, vb0);
+    issue_k(min(2, n - 1), kb2);
+    issue_v(min(1, n - 1), vb1);
+    wait_older_copies();
+    lds_barrier();
+
+    // step t: scores of t+1 from kn, P*V of t from vc; K(t+3) -> ki, V(t+2) -> vi
+    auto step = [&](int t, const char* kn, const char* vc, char* ki, char* vi) __attribute__((always_inline)) {
+        issue_k(min(t + 3, n - 1), ki);
+        issue_v(min(t + 2, n - 1), vi);
+        softmax_head(scur);
+        f32x16_t snext[2];
+        // past the last tile the score block reads stale data and is discarded
+        tile_work(std::true_type{}, std::true_type{}, scur, snext, kn, vc);
+        if (t + 1 < n) mask_tile(t + 1, snext);
+        scur[0] = snext[0];
+        scur[1] = snext[1];
+        wait_older_copies();
+        lds_barrier();
+    };
+    for (int t = 0; t < n; t += 3) {
+        // (already true here; stated so that the compiler's own copy
+        // tracking does not lose it at the loop head)
+        wait_older_copies();
+        step(t, kb1, vb0, kb0, vb2);
+        if (t + 1 < n) step(t + 1, kb2, vb1, kb1, vb0);
+        if (t + 2 < n) step(t + 2, kb0, vb2, kb2, vb1);
+    }
+    // no copy may still be writing this workgroup's LDS when it ends
+    __builtin_amdgcn_s_waitcnt(0xF70);
+
+    const float lt = partner_sum(l_run);
+    if (!wave_live || qi >= N) return;
+    const float inv = 1.f / lt;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int quad = 0; quad < 4; ++quad) {
+            const int d0 = db * 32 + 8 * quad + 4 * g;
+            typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+            const bf16x4_t o = {(__bf16)(oacc[db][4 * quad + 0] * inv), (__bf16)(oacc[db][4 * quad + 1] * inv),
+                                (__bf16)(oacc[db][4 * quad + 2] * inv), (__bf16)(oacc[db][4 * quad + 3] * inv)};
+            *(bf16x4_t*)(og + (size_t)qi * D + d0) = o;
+        }
+}
+
 template <bool BF, int D, int MODE>
 hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
+    if constexpr (BF && MODE != kStrided) {
+        if (p.HG * p.PB == 8) {
+            hipLaunchKernelGGL((band8_kernel<D, MODE>), dim3(p.total), dim3(kThreads8), 0, s, p);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((band_fwd_kernel<BF, D, MODE>), dim3(p.total), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }

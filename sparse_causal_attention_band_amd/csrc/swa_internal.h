@@ -43,6 +43,24 @@ hipError_t launch_ring_append(int elem_bytes, int d, const void* k, const void* 
 constexpr int kQueriesPerWave = 32;
 constexpr int kKeysPerTile = 64;
 
+// Waves per workgroup of the band kernels.  Every wave of a workgroup walks
+// the key tiles of all its rows, so a workgroup should span few positions:
+// bf16 band and chunk modes with at least four query heads per KV head run
+// 8 waves (4 heads x 64 positions), everything else 4 waves.
+inline int waves_per_group(bool bf16, bool strided, int G) { return bf16 && !strided && G % 4 == 0 ? 8 : 4; }
+
+// Split a workgroup's waves into HG query heads (of one KV head) times PB
+// blocks of 32 positions: HG is the largest power of two <= waves dividing G.
+inline void set_wave_split(PrefillParams& p, int waves, int rows) {
+    int hg = 1;
+    while (hg * 2 <= waves && p.G % (hg * 2) == 0) hg *= 2;
+    p.HG = hg;
+    p.PB = waves / hg;
+    const int BM = kQueriesPerWave * p.PB;
+    p.nqb = (rows + BM - 1) / BM;
+    p.ngroups = p.G / hg;
+}
+
 // ---------------------------------------------------------------- decode
 struct DecodeParams {
     const void* q;
