@@ -14,4 +14,6 @@ from .swa_oracle import (  # noqa: F401
     ring_slot,
     ring_append,
     chunk_prefill,
+    allowed_mask_two_sided,
+    attn_fwd_two_sided,
 )

@@ -28,6 +28,12 @@ Everything here is the plain definition, written out in float64 with numpy:
   windows, so each row attends to the cached history in the ring plus the
   chunk's own earlier rows, under the same band; the history is read before
   the chunk is written into the ring.
+* The two-sided (bidirectional) band drops the causal cut: row i reads keys
+  i-left .. i+right, clipped to the sequence.  The attention-variants page
+  (概念, 滑动窗口注意力) gives [i - W/2, i + W/2]; the SWA page (§3.1 and its
+  §3.3 example) gives [i - w, i + w] with a radius w and builds the mask as
+  start = max(0, i-w), end = min(n, i+w+1).  Separate left and right radii
+  cover both; right = 0 is the causal band with W = left + 1.
 
 Readings where the pages leave a step open (each one is also listed in the
 design notes of the repository):
@@ -61,6 +67,8 @@ __all__ = [
     "attn_fwd_parallel",
     "ring_append",
     "chunk_prefill",
+    "allowed_mask_two_sided",
+    "attn_fwd_two_sided",
 ]
 
 
@@ -350,4 +358,48 @@ def chunk_prefill(q, k, v, kring, vring, p0, window: int, scale: Optional[float]
             vv = np.concatenate([vring[b, g][slots], v[b, g]])
             qq = np.concatenate([np.zeros((n_hist, d)), q[b, h]])
             out[b, h] = _head_rows(qq, kk, vv, n_hist + sel, window, 0, scale)
+    return out
+
+
+def allowed_mask_two_sided(n: int, left: int, right: int) -> np.ndarray:
+    """Boolean n x n matrix of the two-sided band: key j is allowed for row i
+    iff i - left <= j <= i + right (0-based, clipped to [0, n))."""
+    if left < 0 or right < 0:
+        raise ValueError("left and right must be >= 0")
+    m = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        m[i, max(0, i - left):min(n, i + right + 1)] = True
+    return m
+
+
+def attn_fwd_two_sided(q, k, v, left: int, right: int, scale: Optional[float] = None) -> np.ndarray:
+    """softmax(scale * Q K^T + M) V with the two-sided band mask M (no causal
+    cut), float64 [B, Hq, N, d].  Rows are taken in blocks; each row
+    normalises over exactly its own keys i-left .. i+right."""
+    if left < 0 or right < 0:
+        raise ValueError("left and right must be >= 0")
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, Hq, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or v.shape != k.shape or Hq % k.shape[1] != 0:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hq a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    G = Hq // k.shape[1]
+    out = np.empty((B, Hq, N, v.shape[3]), dtype=np.float64)
+    block = 256
+    for b in range(B):
+        for h in range(Hq):
+            kk_all = np.asarray(k[b, h // G], dtype=np.float64)
+            vv_all = np.asarray(v[b, h // G], dtype=np.float64)
+            qq_all = np.asarray(q[b, h], dtype=np.float64)
+            for i0 in range(0, N, block):
+                i1 = min(N, i0 + block) - 1
+                lo, hi = max(0, i0 - left), min(N - 1, i1 + right)
+                rows = np.arange(i0, i1 + 1)
+                keys = np.arange(lo, hi + 1)
+                allowed = (keys[None, :] >= rows[:, None] - left) & (keys[None, :] <= rows[:, None] + right)
+                scores = scale * (qq_all[i0:i1 + 1] @ kk_all[lo:hi + 1].T)
+                out[b, h, i0:i1 + 1] = _masked_softmax_rows(scores, allowed) @ vv_all[lo:hi + 1]
     return out

@@ -413,3 +413,85 @@ def test_planted_mistakes_are_caught(monkeypatch):
         assert _pins_fail(monkeypatch, "_head_rows", head_rows_k_for_v)
     finally:
         del swa_oracle._head_rows_orig
+
+
+# ---------------------------------------------------------------- two-sided band
+def _page_two_sided_mask(n, w):
+    """The SWA page's §3.3 construction, restated: ones, then zero the
+    columns before max(0, i-w) and from min(n, i+w+1) on, row by row."""
+    m = np.ones((n, n))
+    for i in range(n):
+        start = max(0, i - w)
+        end = min(n, i + w + 1)
+        m[i, :start] = 0
+        m[i, end:] = 0
+    return m.astype(bool)
+
+
+@pytest.mark.parametrize("n,w", [(8, 2), (13, 4), (5, 0), (9, 20)])
+def test_two_sided_mask_matches_the_page_construction(n, w):
+    assert np.array_equal(oracle.allowed_mask_two_sided(n, w, w), _page_two_sided_mask(n, w))
+    # and the page's causal combination (times the lower triangle) is the
+    # causal band with W = w + 1
+    causal = _page_two_sided_mask(n, w) & np.tril(np.ones((n, n), dtype=bool))
+    assert np.array_equal(causal, oracle.allowed_mask(n, w + 1))
+
+
+@pytest.mark.parametrize("n,left,right", [(17, 3, 5), (40, 0, 7), (33, 12, 0), (10, 30, 30)])
+def test_two_sided_pair_count_closed_form(n, left, right):
+    want = sum(min(i, left) + min(n - 1 - i, right) + 1 for i in range(n))
+    assert int(oracle.allowed_mask_two_sided(n, left, right).sum()) == want
+
+
+def test_two_sided_with_no_right_part_is_the_causal_band():
+    rng = np.random.default_rng(21)
+    q, k, v = (rng.standard_normal((1, 4, 70, 8)) for _ in range(3))
+    k, v = k[:, :2], v[:, :2]
+    for left in (0, 1, 6, 69, 200):
+        got = oracle.attn_fwd_two_sided(q, k, v, left, 0)
+        want = oracle.attn_fwd(q, k, v, left + 1)
+        assert np.abs(got - want).max() <= 1e-13
+
+
+def test_two_sided_full_width_is_sdpa_without_mask():
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((2, 4, 45, 16))
+    k = rng.standard_normal((2, 4, 45, 16))
+    v = rng.standard_normal((2, 4, 45, 16))
+    got = oracle.attn_fwd_two_sided(q, k, v, 44, 44)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v)).numpy()
+    assert np.abs(got - want).max() <= 1e-12
+
+
+def test_two_sided_sdpa_with_boolean_band():
+    rng = np.random.default_rng(23)
+    q, k, v = (rng.standard_normal((1, 2, 64, 8)) for _ in range(3))
+    m = torch.from_numpy(oracle.allowed_mask_two_sided(64, 5, 11))
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=m).numpy()
+    assert np.abs(oracle.attn_fwd_two_sided(q, k, v, 5, 11) - want).max() <= 1e-12
+
+
+def test_two_sided_reversal_swaps_left_and_right():
+    """Reversing the positions turns the band i-left..i+right into
+    i-right..i+left: a swapped pair of radii fails this."""
+    rng = np.random.default_rng(24)
+    q, k, v = (rng.standard_normal((1, 1, 50, 6)) for _ in range(3))
+    a = oracle.attn_fwd_two_sided(q, k, v, 3, 9)
+    r = oracle.attn_fwd_two_sided(q[:, :, ::-1], k[:, :, ::-1], v[:, :, ::-1], 9, 3)[:, :, ::-1]
+    assert np.abs(a - r).max() <= 1e-13
+    assert np.abs(a - oracle.attn_fwd_two_sided(q, k, v, 9, 3)).max() > 1e-3
+
+
+def test_two_sided_brute_force():
+    rng = np.random.default_rng(25)
+    n, d, left, right = 11, 3, 2, 4
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    got = oracle.attn_fwd_two_sided(q[None, None], k[None, None], v[None, None], left, right, 0.7)[0, 0]
+    for i in range(n):
+        keys = [j for j in range(n) if i - left <= j <= i + right]
+        w = [math.exp(0.7 * sum(q[i, c] * k[j, c] for c in range(d))) for j in keys]
+        z = sum(w)
+        want = [sum(w[a] * v[j, c] for a, j in enumerate(keys)) / z for c in range(d)]
+        assert max(abs(got[i, c] - want[c]) for c in range(d)) <= 1e-12
