@@ -114,6 +114,24 @@ SWA_API int swa_decode_f32(const float* q, const float* kring, const float* vrin
                    void* workspace, size_t workspace_bytes, int window, hipStream_t stream);
 
 /*
+ * Two-sided (bidirectional) band, no causal cut: row i reads keys
+ * i-left .. i+right (clipped to [0, N)).  The attention-variants page
+ * (概念, 滑动窗口注意力) gives the bidirectional window [i - W/2, i + W/2];
+ * the SWA page (§3.1, §3.3) gives [i - w, i + w] with a radius w; separate
+ * radii cover both.  right = 0 gives the same result as swa_attn_fwd with
+ * window = left + 1.
+ *   q, out : [B, Hq, N, d]   k, v : [B, Hkv, N, d]   (as swa_attn_fwd)
+ *   left, right >= 0 (values >= N act as N - 1); other arguments, layouts,
+ *   ownership and errors as swa_attn_fwd.
+ */
+SWA_API int swa_attn_fwd_two_sided(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv,
+                                   int N, int d, int left, int right, float scale, hipStream_t stream);
+
+/* Same contract with fp32 tensors and fp32 matrix-core arithmetic. */
+SWA_API int swa_attn_fwd_two_sided_f32(const float* q, const float* k, const float* v, float* out, int B, int Hq,
+                                       int Hkv, int N, int d, int left, int right, float scale, hipStream_t stream);
+
+/*
  * Chunked prefill over the rolling cache (page "SWA：滑动窗口注意力与跨层信息传递",
  * §4.3): a chunk of T new tokens attends to the cached history plus its own
  * earlier rows, each row under its own band.  Chunk row r of sequence b is

@@ -1,15 +1,18 @@
 """Causal sliding-window attention for MI355X (gfx950).
 
 Python face of ``libswa_attn.so``: ``attn_fwd`` (band + optional strided
-keys, whole-sequence forward) and ``decode`` (one token per sequence over a
-rolling window-slot KV cache).  The arithmetic runs in hand-written HIP
-kernels behind the C ABI declared in ``include/swa_attn.h``.
+keys, whole-sequence forward), ``attn_fwd_two_sided`` (band without the
+causal cut), ``decode`` (one token per sequence over a rolling window-slot KV
+cache), ``chunk_prefill`` and ``ring_append`` (prefill in chunks over that
+cache).  The arithmetic runs in hand-written HIP kernels behind the C ABI
+declared in ``include/swa_attn.h``.
 """
 from ._lib import (  # noqa: F401
     LIB_PATH,
     SIGNATURES,
     SwaError,
     attn_fwd,
+    attn_fwd_two_sided,
     chunk_prefill,
     decode,
     decode_workspace_bytes,

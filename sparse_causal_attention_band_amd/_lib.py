@@ -32,6 +32,8 @@ SIGNATURES = {
     "swa_attn_fwd_f32": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _Z, _I, _P]),
     "swa_decode_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _Z, _I, _P]),
+    "swa_attn_fwd_two_sided": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "swa_attn_fwd_two_sided_f32": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_chunk_prefill": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_chunk_prefill_f32": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_ring_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
@@ -118,6 +120,37 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: int, str
     fn = lib().swa_attn_fwd if dtype == torch.bfloat16 else lib().swa_attn_fwd_f32
     _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, k.shape[1], N, d,
               int(window), int(stride), float(scale), _stream(dev)))
+    return out
+
+
+def attn_fwd_two_sided(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, left: int, right: int,
+                       scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Two-sided band attention (no causal cut): row i reads keys i-left .. i+right.
+
+    Shapes, dtypes and device as ``attn_fwd``.
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    dtype, dev = q.dtype, q.device
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bfloat16 or float32")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dtype, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    fn = lib().swa_attn_fwd_two_sided if dtype == torch.bfloat16 else lib().swa_attn_fwd_two_sided_f32
+    _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, k.shape[1], N, d,
+              int(left), int(right), float(scale), _stream(dev)))
     return out
 
 

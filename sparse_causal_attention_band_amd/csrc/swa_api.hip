@@ -40,9 +40,11 @@ int check_scale(const char* name, float scale) {
     return SWA_OK;
 }
 
-int attn_fwd(bool bf16, const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N,
-             int d, int window, int stride, float scale, hipStream_t stream) {
-    const char* name = bf16 ? "swa_attn_fwd" : "swa_attn_fwd_f32";
+// Band forward shared by the causal entry points (right = 0) and the
+// two-sided ones (stride = 0): row i reads keys max(0, i-window+1) ..
+// min(N-1, i+right), plus the multiples of stride below the band.
+int band_fwd(bool bf16, const char* name, const void* q, const void* k, const void* v, void* out, int B, int Hq,
+             int Hkv, int N, int d, int window, int right, int stride, float scale, hipStream_t stream) {
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1)
         return fail(SWA_ERR_INVALID_ARG, "%s: B, N, Hq, Hkv must be >= 1 (B=%d N=%d Hq=%d Hkv=%d)", name, B, N, Hq,
                     Hkv);
@@ -79,6 +81,7 @@ int attn_fwd(bool bf16, const void* q, const void* k, const void* v, void* out, 
     p.Hkv = Hkv;
     p.N = N;
     p.W = window < N ? window : N;  // W >= N is full causal: identical work and bits
+    p.wr = right < N ? right : N - 1;
     p.stride = stride > 0 ? stride : 0;
     p.c = fabsf(scale) * kLog2e;
     p.neg = scale < 0.f;
@@ -90,6 +93,21 @@ int attn_fwd(bool bf16, const void* q, const void* k, const void* v, void* out, 
     hipError_t e = swa::launch_band_fwd(bf16, d, p.stride > 0 ? swa::kStrided : swa::kBand, p, stream);
     if (e != hipSuccess) return fail(SWA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
     return ok();
+}
+
+int attn_fwd(bool bf16, const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N,
+             int d, int window, int stride, float scale, hipStream_t stream) {
+    return band_fwd(bf16, bf16 ? "swa_attn_fwd" : "swa_attn_fwd_f32", q, k, v, out, B, Hq, Hkv, N, d, window, 0,
+                    stride, scale, stream);
+}
+
+int two_sided_fwd(bool bf16, const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N,
+                  int d, int left, int right, float scale, hipStream_t stream) {
+    const char* name = bf16 ? "swa_attn_fwd_two_sided" : "swa_attn_fwd_two_sided_f32";
+    if (left < 0 || right < 0)
+        return fail(SWA_ERR_INVALID_ARG, "%s: left and right must be >= 0 (got %d, %d)", name, left, right);
+    const int window = left < N ? left + 1 : (N > 0 ? N : 1);
+    return band_fwd(bf16, name, q, k, v, out, B, Hq, Hkv, N, d, window, right, 0, scale, stream);
 }
 
 int chunk_prefill(bool bf16, const void* q, const void* k, const void* v, const void* kring, const void* vring,
@@ -122,6 +140,7 @@ int chunk_prefill(bool bf16, const void* q, const void* k, const void* v, const 
     p.Hkv = Hkv;
     p.N = T;
     p.W = window;  // the ring size; the kernel clamps the band to the keys it has
+    p.wr = 0;
     p.stride = 0;
     p.c = fabsf(scale) * kLog2e;
     p.neg = scale < 0.f;
@@ -221,6 +240,16 @@ int swa_decode_f32(const float* q, const float* kring, const float* vring, const
                    int Hq, int Hkv, int d, float scale, void* workspace, size_t workspace_bytes, int window,
                    hipStream_t stream) {
     return decode(false, q, kring, vring, pos, out, B, Hq, Hkv, d, scale, workspace, workspace_bytes, window, stream);
+}
+
+int swa_attn_fwd_two_sided(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N,
+                           int d, int left, int right, float scale, hipStream_t stream) {
+    return two_sided_fwd(true, q, k, v, out, B, Hq, Hkv, N, d, left, right, scale, stream);
+}
+
+int swa_attn_fwd_two_sided_f32(const float* q, const float* k, const float* v, float* out, int B, int Hq, int Hkv,
+                               int N, int d, int left, int right, float scale, hipStream_t stream) {
+    return two_sided_fwd(false, q, k, v, out, B, Hq, Hkv, N, d, left, right, scale, stream);
 }
 
 int swa_chunk_prefill(const void* q, const void* k, const void* v, const void* kring, const void* vring,

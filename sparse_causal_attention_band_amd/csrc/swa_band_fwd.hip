@@ -183,7 +183,8 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
 
     // ---- key tiles of this workgroup: band tiles kt_hi .. kt_lo, then the
     // compact strided tiles (keys m*stride < kt_lo*64, read by every row).
-    const int kt_hi = min(NK - 1, qoff + q0 + BM - 1) / kTileN;
+    const int wr = p.wr;  // right radius of a two-sided band (0: causal)
+    const int kt_hi = min(NK - 1, qoff + q0 + BM - 1 + wr) / kTileN;
     const int kt_lo = max(0, qoff + q0 - W + 1) / kTileN;
     const int nband = kt_hi - kt_lo + 1;
     int M = 0, ncomp = 0;
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     auto mask_tile = [&](int t, f32x16_t* sc) __attribute__((always_inline)) {
         const bool band = t < nband;
         const int j0 = (kt_hi - t) * kTileN;
-        const bool edge = band ? !(j0 + kTileN - 1 <= qvw0 && j0 >= qvw0 + kQw - W)
+        const bool edge = band ? !(j0 + kTileN - 1 <= qvw0 + wr && j0 >= qvw0 + kQw - W && j0 + kTileN <= NK)
                                : ((t - nband + 1) * kTileN > M);
         if (edge) {
             // bit o of smask: key j0 + o is a multiple of the stride
@@ -324,7 +325,10 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
                     // no per-element divergent branches
                     const int r = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
                     const int dist = qv - (j0 + r);
-                    const bool in_band = (dist >= 0) & ((dist < W) | (STRIDED & (((smask >> r) & 1ull) != 0)));
+                    // (keys past the end exist only as clamped copies of
+                    // the last row; causal rows never reach them)
+                    const bool in_band = (dist >= -wr) & (j0 + r < NK) &
+                                         ((dist < W) | (STRIDED & (((smask >> r) & 1ull) != 0)));
                     const bool in_comp = (t - nband) * kTileN + r < M;
                     sc[kb][i] = (band ? in_band : in_comp) ? sc[kb][i] : -INFINITY;
                 }
@@ -561,7 +565,8 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     const elem_t* krg = CHUNK ? (const elem_t*)p.kring + ring_head : nullptr;
     const elem_t* vrg = CHUNK ? (const elem_t*)p.vring + ring_head : nullptr;
 
-    const int kt_hi = min(NK - 1, qoff + q0 + BM - 1) / kTileN;
+    const int wr = p.wr;  // right radius of a two-sided band (0: causal)
+    const int kt_hi = min(NK - 1, qoff + q0 + BM - 1 + wr) / kTileN;
     const int kt_lo = max(0, qoff + q0 - W + 1) / kTileN;
     const int nband = kt_hi - kt_lo + 1;
     int M = 0, ncomp = 0;
@@ -704,7 +709,8 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     auto mask_tile = [&](int t, f32x16_t* sc) __attribute__((always_inline)) {
         const bool band = t < nband;
         const int j0 = (kt_hi - t) * kTileN;
-        const bool edge = band ? !(j0 + kTileN - 1 <= qvw0 && j0 >= qvw0 + kQw - W) : ((t - nband + 1) * kTileN > M);
+        const bool edge = band ? !(j0 + kTileN - 1 <= qvw0 + wr && j0 >= qvw0 + kQw - W && j0 + kTileN <= NK)
+                               : ((t - nband + 1) * kTileN > M);
         if (edge) {
             uint64_t smask = 0;
             if (STRIDED && band) {
@@ -717,7 +723,10 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
                 for (int i = 0; i < 16; ++i) {
                     const int r = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
                     const int dist = qv - (j0 + r);
-                    const bool in_band = (dist >= 0) & ((dist < W) | (STRIDED & (((smask >> r) & 1ull) != 0)));
+                    // (keys past the end exist only as clamped copies of
+                    // the last row; causal rows never reach them)
+                    const bool in_band = (dist >= -wr) & (j0 + r < NK) &
+                                         ((dist < W) | (STRIDED & (((smask >> r) & 1ull) != 0)));
                     const bool in_comp = (t - nband) * kTileN + r < M;
                     sc[kb][i] = (band ? in_band : in_comp) ? sc[kb][i] : -INFINITY;
                 }

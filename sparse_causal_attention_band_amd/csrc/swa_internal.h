@@ -21,6 +21,7 @@ struct PrefillParams {
     const int32_t* p0;     // chunk mode: [B] positions already cached
     int B, Hq, Hkv, N;
     int W;        // window (band modes: clamped to N; chunk mode: the ring size)
+    int wr;       // two-sided band: keys up to i + wr are read too (0: causal)
     int stride;   // > 0 only for the strided instantiation
     float c;      // |scale| * log2(e): scores are kept in the log2 domain
     int neg;      // scale < 0: queries enter with flipped sign (exact)
