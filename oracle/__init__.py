@@ -16,4 +16,5 @@ from .swa_oracle import (  # noqa: F401
     chunk_prefill,
     allowed_mask_two_sided,
     attn_fwd_two_sided,
+    diff_attn_fwd,
 )

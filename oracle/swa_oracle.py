@@ -35,6 +35,11 @@ Everything here is the plain definition, written out in float64 with numpy:
   start = max(0, i-w), end = min(n, i+w+1).  Separate left and right radii
   cover both; right = 0 is the causal band with W = left + 1.
 
+* Differential attention (attention-variants page, 概念 and 第 4 步): two
+  attention maps from separate Q/K pairs over one V, out = (A1 - lam * A2) V
+  with a scalar lam per query head.  Here both maps use the same sliding-window
+  band; with W >= N this is the page's causal version.
+
 Readings where the pages leave a step open (each one is also listed in the
 design notes of the repository):
 
@@ -69,6 +74,7 @@ __all__ = [
     "chunk_prefill",
     "allowed_mask_two_sided",
     "attn_fwd_two_sided",
+    "diff_attn_fwd",
 ]
 
 
@@ -402,4 +408,36 @@ def attn_fwd_two_sided(q, k, v, left: int, right: int, scale: Optional[float] = 
                 allowed = (keys[None, :] >= rows[:, None] - left) & (keys[None, :] <= rows[:, None] + right)
                 scores = scale * (qq_all[i0:i1 + 1] @ kk_all[lo:hi + 1].T)
                 out[b, h, i0:i1 + 1] = _masked_softmax_rows(scores, allowed) @ vv_all[lo:hi + 1]
+    return out
+
+
+def diff_attn_fwd(q1, k1, q2, k2, v, lam, window: int, scale: Optional[float] = None) -> np.ndarray:
+    """Differential sliding-window attention, float64 [B, Hq, N, d]:
+    (A1 - lam[h] * A2) V with A1 = softmax(scale Q1 K1^T + M), A2 the same
+    for (Q2, K2), M the causal band of width W, and lam an array of Hq
+    scalars (attention-variants page, 第 4 步).  The difference of the two
+    probability matrices is formed first, then multiplied by V."""
+    q1, k1, q2, k2, v = (np.asarray(x) for x in (q1, k1, q2, k2, v))
+    lam = np.asarray(lam, dtype=np.float64).reshape(-1)
+    B, Hq, N, d = q1.shape
+    if q2.shape != q1.shape or k1.shape != k2.shape or v.shape[:3] != k1.shape[:3] or lam.shape != (Hq,):
+        raise ValueError("q1/q2, k1/k2/v or lam shapes do not match")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    G = Hq // k1.shape[1]
+    out = np.empty((B, Hq, N, v.shape[3]), dtype=np.float64)
+    block = 256
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for i0 in range(0, N, block):
+                i1 = min(N, i0 + block) - 1
+                rows = np.arange(i0, i1 + 1, dtype=np.int64)
+                keys = _block_keys(i0, i1, window, 0)
+                allowed = _row_allowed(rows, keys, window, 0)
+                a1 = _masked_softmax_rows(scale * (np.asarray(q1[b, h, i0:i1 + 1], np.float64)
+                                                   @ np.asarray(k1[b, g][keys], np.float64).T), allowed)
+                a2 = _masked_softmax_rows(scale * (np.asarray(q2[b, h, i0:i1 + 1], np.float64)
+                                                   @ np.asarray(k2[b, g][keys], np.float64).T), allowed)
+                out[b, h, i0:i1 + 1] = (a1 - lam[h] * a2) @ np.asarray(v[b, g][keys], np.float64)
     return out

@@ -495,3 +495,49 @@ def test_two_sided_brute_force():
         z = sum(w)
         want = [sum(w[a] * v[j, c] for a, j in enumerate(keys)) / z for c in range(d)]
         assert max(abs(got[i, c] - want[c]) for c in range(d)) <= 1e-12
+
+
+# ---------------------------------------------------------------- differential attention
+def _diff_inputs(seed, B=1, Hq=4, Hkv=2, N=90, d=8):
+    rng = np.random.default_rng(seed)
+    q1, q2 = (rng.standard_normal((B, Hq, N, d)) for _ in range(2))
+    k1, k2, v = (rng.standard_normal((B, Hkv, N, d)) for _ in range(3))
+    lam = rng.uniform(0.5, 0.8, Hq)  # the range the pages quote for the learned scalar
+    return q1, k1, q2, k2, v, lam
+
+
+def test_diff_with_zero_lambda_is_the_first_map():
+    q1, k1, q2, k2, v, lam = _diff_inputs(31)
+    got = oracle.diff_attn_fwd(q1, k1, q2, k2, v, np.zeros(4), 17)
+    assert np.abs(got - oracle.attn_fwd(q1, k1, v, 17)).max() <= 1e-13
+
+
+def test_diff_is_affine_in_lambda_with_the_second_map_as_slope():
+    q1, k1, q2, k2, v, lam = _diff_inputs(32)
+    got = oracle.diff_attn_fwd(q1, k1, q2, k2, v, lam, 25)
+    want = oracle.attn_fwd(q1, k1, v, 25) - lam[None, :, None, None] * oracle.attn_fwd(q2, k2, v, 25)
+    assert np.abs(got - want).max() <= 1e-13
+
+
+def test_diff_of_identical_maps_scales_by_one_minus_lambda():
+    q1, k1, _, _, v, lam = _diff_inputs(33)
+    got = oracle.diff_attn_fwd(q1, k1, q1, k1, v, lam, 9)
+    want = (1 - lam)[None, :, None, None] * oracle.attn_fwd(q1, k1, v, 9)
+    assert np.abs(got - want).max() <= 1e-13
+
+
+def test_diff_brute_force_page_causal_form():
+    """W >= N: the page's two causal softmax maps, subtracted, times V."""
+    rng = np.random.default_rng(34)
+    n, d, lam = 7, 3, 0.65
+    q1, k1, q2, k2, v = (rng.standard_normal((n, d)) for _ in range(5))
+    got = oracle.diff_attn_fwd(q1[None, None], k1[None, None], q2[None, None], k2[None, None], v[None, None],
+                               [lam], n)[0, 0]
+    sd = math.sqrt(d)
+    for i in range(n):
+        w1 = [math.exp(sum(q1[i, c] * k1[j, c] for c in range(d)) / sd) for j in range(i + 1)]
+        w2 = [math.exp(sum(q2[i, c] * k2[j, c] for c in range(d)) / sd) for j in range(i + 1)]
+        z1, z2 = sum(w1), sum(w2)
+        for c in range(d):
+            want = sum((w1[j] / z1 - lam * w2[j] / z2) * v[j, c] for j in range(i + 1))
+            assert abs(got[i, c] - want) <= 1e-12
