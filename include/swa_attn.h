@@ -132,6 +132,28 @@ SWA_API int swa_attn_fwd_two_sided_f32(const float* q, const float* k, const flo
                                        int Hkv, int N, int d, int left, int right, float scale, hipStream_t stream);
 
 /*
+ * Differential sliding-window attention (attention-variants page, 概念 and
+ * 第 4 步): out = (A1 - lam[h] * A2) V, where A1 and A2 are the causal
+ * sliding-window softmax maps of (q1, k1) and (q2, k2) over the same band
+ * and the same V, and lam holds one scalar per query head.
+ *   q1, q2, out : [B, Hq, N, d]   k1, k2, v : [B, Hkv, N, d]
+ *   lam : fp32 [Hq] on the device
+ *   window, scale, d, alignment and errors as swa_attn_fwd.
+ * Runs as two launches of the band kernel on `stream`: the first writes
+ * A1 V to out, the second subtracts lam * A2 V from it in its epilogue (in
+ * the bf16 entry point A1 V is therefore rounded to bf16 once before the
+ * subtraction).  out must not overlap any input.
+ */
+SWA_API int swa_diff_attn_fwd(const void* q1, const void* k1, const void* q2, const void* k2, const void* v,
+                              const float* lam, void* out, int B, int Hq, int Hkv, int N, int d, int window,
+                              float scale, hipStream_t stream);
+
+/* Same contract with fp32 tensors and fp32 matrix-core arithmetic. */
+SWA_API int swa_diff_attn_fwd_f32(const float* q1, const float* k1, const float* q2, const float* k2,
+                                  const float* v, const float* lam, float* out, int B, int Hq, int Hkv, int N, int d,
+                                  int window, float scale, hipStream_t stream);
+
+/*
  * Chunked prefill over the rolling cache (page "SWA：滑动窗口注意力与跨层信息传递",
  * §4.3): a chunk of T new tokens attends to the cached history plus its own
  * earlier rows, each row under its own band.  Chunk row r of sequence b is

@@ -2,7 +2,8 @@
 
 Python face of ``libswa_attn.so``: ``attn_fwd`` (band + optional strided
 keys, whole-sequence forward), ``attn_fwd_two_sided`` (band without the
-causal cut), ``decode`` (one token per sequence over a rolling window-slot KV
+causal cut), ``diff_attn_fwd`` (differential attention over the band),
+``decode`` (one token per sequence over a rolling window-slot KV
 cache), ``chunk_prefill`` and ``ring_append`` (prefill in chunks over that
 cache).  The arithmetic runs in hand-written HIP kernels behind the C ABI
 declared in ``include/swa_attn.h``.
@@ -16,6 +17,7 @@ from ._lib import (  # noqa: F401
     chunk_prefill,
     decode,
     decode_workspace_bytes,
+    diff_attn_fwd,
     lib,
     ring_append,
 )

@@ -34,6 +34,8 @@ SIGNATURES = {
     "swa_decode_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _Z, _I, _P]),
     "swa_attn_fwd_two_sided": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_attn_fwd_two_sided_f32": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "swa_diff_attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "swa_diff_attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_chunk_prefill": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_chunk_prefill_f32": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_ring_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
@@ -151,6 +153,42 @@ def attn_fwd_two_sided(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, left: 
     fn = lib().swa_attn_fwd_two_sided if dtype == torch.bfloat16 else lib().swa_attn_fwd_two_sided_f32
     _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, k.shape[1], N, d,
               int(left), int(right), float(scale), _stream(dev)))
+    return out
+
+
+def diff_attn_fwd(q1: torch.Tensor, k1: torch.Tensor, q2: torch.Tensor, k2: torch.Tensor, v: torch.Tensor,
+                  lam: torch.Tensor, window: int, scale: float | None = None,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """Differential sliding-window attention: (A1 - lam[h] * A2) V.
+
+    q1, q2: [B, Hq, N, d]; k1, k2, v: [B, Hkv, N, d]; lam: float32 [Hq] on
+    the GPU.  All bf16 (or all fp32).
+    """
+    if q1.dim() != 4 or q2.shape != q1.shape or k1.dim() != 4 or k2.shape != k1.shape or v.shape != k1.shape:
+        raise ValueError("q1/q2 must be [B, Hq, N, d] and k1/k2/v [B, Hkv, N, d]")
+    B, Hq, N, d = q1.shape
+    if k1.shape[0] != B or k1.shape[2] != N or k1.shape[3] != d:
+        raise ValueError("k1, k2, v do not match q1")
+    dtype, dev = q1.dtype, q1.device
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q1 must be bfloat16 or float32")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    for t, n in ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v")):
+        _need(t, n, dtype, dev)
+    _need(lam, "lam", torch.float32, dev)
+    if lam.shape != (Hq,):
+        raise ValueError("lam must be [Hq]")
+    if out is None:
+        out = torch.empty_like(q1)
+    _need(out, "out", dtype, dev)
+    if out.shape != q1.shape:
+        raise ValueError("out must have q1's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    fn = lib().swa_diff_attn_fwd if dtype == torch.bfloat16 else lib().swa_diff_attn_fwd_f32
+    _check(fn(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(), lam.data_ptr(),
+              out.data_ptr(), B, Hq, k1.shape[1], N, d, int(window), float(scale), _stream(dev)))
     return out
 
 

@@ -44,7 +44,8 @@ int check_scale(const char* name, float scale) {
 // two-sided ones (stride = 0): row i reads keys max(0, i-window+1) ..
 // min(N-1, i+right), plus the multiples of stride below the band.
 int band_fwd(bool bf16, const char* name, const void* q, const void* k, const void* v, void* out, int B, int Hq,
-             int Hkv, int N, int d, int window, int right, int stride, float scale, hipStream_t stream) {
+             int Hkv, int N, int d, int window, int right, int stride, float scale, hipStream_t stream,
+             const float* lam = nullptr) {
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1)
         return fail(SWA_ERR_INVALID_ARG, "%s: B, N, Hq, Hkv must be >= 1 (B=%d N=%d Hq=%d Hkv=%d)", name, B, N, Hq,
                     Hkv);
@@ -76,6 +77,7 @@ int band_fwd(bool bf16, const char* name, const void* q, const void* k, const vo
     p.kring = nullptr;
     p.vring = nullptr;
     p.p0 = nullptr;
+    p.lam = lam;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
@@ -110,6 +112,30 @@ int two_sided_fwd(bool bf16, const void* q, const void* k, const void* v, void* 
     return band_fwd(bf16, name, q, k, v, out, B, Hq, Hkv, N, d, window, right, 0, scale, stream);
 }
 
+// Differential attention: the first map's result is written to out, then
+// the second launch subtracts lam[h] times its own result in its epilogue.
+int diff_fwd(bool bf16, const void* q1, const void* k1, const void* q2, const void* k2, const void* v,
+             const float* lam, void* out, int B, int Hq, int Hkv, int N, int d, int window, float scale,
+             hipStream_t stream) {
+    const char* name = bf16 ? "swa_diff_attn_fwd" : "swa_diff_attn_fwd_f32";
+    if (lam == nullptr || ((uintptr_t)lam & 3u))
+        return fail(SWA_ERR_INVALID_ARG, "%s: lam must be non-null, 4-byte aligned", name);
+    if (B >= 1 && N >= 1 && Hq >= 1 && Hkv >= 1 && d >= 1) {
+        const long long es = bf16 ? 2 : 4;
+        const long long qbytes = (long long)B * Hq * N * d * es;
+        const long long kbytes = (long long)B * Hkv * N * d * es;
+        const char* o = (const char*)out;
+        auto hits = [&](const void* a, long long na) {
+            const char* x = (const char*)a;
+            return x < o + qbytes && o < x + na;
+        };
+        if (hits(q2, qbytes) || hits(k2, kbytes) || hits(lam, (long long)Hq * 4))
+            return fail(SWA_ERR_INVALID_ARG, "%s: out must not overlap q2, k2 or lam", name);
+    }
+    if (int rc = band_fwd(bf16, name, q1, k1, v, out, B, Hq, Hkv, N, d, window, 0, 0, scale, stream)) return rc;
+    return band_fwd(bf16, name, q2, k2, v, out, B, Hq, Hkv, N, d, window, 0, 0, scale, stream, lam);
+}
+
 int chunk_prefill(bool bf16, const void* q, const void* k, const void* v, const void* kring, const void* vring,
                   const int32_t* p0, void* out, int B, int Hq, int Hkv, int T, int d, int window, float scale,
                   hipStream_t stream) {
@@ -135,6 +161,7 @@ int chunk_prefill(bool bf16, const void* q, const void* k, const void* v, const 
     p.kring = kring;
     p.vring = vring;
     p.p0 = p0;
+    p.lam = nullptr;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
@@ -250,6 +277,17 @@ int swa_attn_fwd_two_sided(const void* q, const void* k, const void* v, void* ou
 int swa_attn_fwd_two_sided_f32(const float* q, const float* k, const float* v, float* out, int B, int Hq, int Hkv,
                                int N, int d, int left, int right, float scale, hipStream_t stream) {
     return two_sided_fwd(false, q, k, v, out, B, Hq, Hkv, N, d, left, right, scale, stream);
+}
+
+int swa_diff_attn_fwd(const void* q1, const void* k1, const void* q2, const void* k2, const void* v, const float* lam,
+                      void* out, int B, int Hq, int Hkv, int N, int d, int window, float scale, hipStream_t stream) {
+    return diff_fwd(true, q1, k1, q2, k2, v, lam, out, B, Hq, Hkv, N, d, window, scale, stream);
+}
+
+int swa_diff_attn_fwd_f32(const float* q1, const float* k1, const float* q2, const float* k2, const float* v,
+                          const float* lam, float* out, int B, int Hq, int Hkv, int N, int d, int window, float scale,
+                          hipStream_t stream) {
+    return diff_fwd(false, q1, k1, q2, k2, v, lam, out, B, Hq, Hkv, N, d, window, scale, stream);
 }
 
 int swa_chunk_prefill(const void* q, const void* k, const void* v, const void* kring, const void* vring,

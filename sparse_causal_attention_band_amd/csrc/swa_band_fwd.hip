@@ -463,22 +463,40 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     // ---- epilogue: O / l, lane holds d = 32*db + 8*quad + 4*g + 0..3
     const float lt = partner_sum(l_run);
     if (!wave_live || qi >= N) return;
-    const float inv = 1.f / lt;
+    // plain store, or (second map of differential attention) out -= lam * O/l
+    const bool sub = p.lam != nullptr;
+    const float inv = (sub ? -p.lam[h] : 1.f) / lt;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int quad = 0; quad < 4; ++quad) {
             const int d0 = db * 32 + 8 * quad + 4 * g;
-            const float o0 = oacc[db][4 * quad + 0] * inv, o1 = oacc[db][4 * quad + 1] * inv;
-            const float o2 = oacc[db][4 * quad + 2] * inv, o3 = oacc[db][4 * quad + 3] * inv;
+            float o0 = oacc[db][4 * quad + 0] * inv, o1 = oacc[db][4 * quad + 1] * inv;
+            float o2 = oacc[db][4 * quad + 2] * inv, o3 = oacc[db][4 * quad + 3] * inv;
             if constexpr (BF) {
                 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                bf16x4_t* dst = (bf16x4_t*)(og + (size_t)qi * D + d0);
+                if (sub) {
+                    const bf16x4_t prev = *dst;
+                    o0 += (float)prev[0];
+                    o1 += (float)prev[1];
+                    o2 += (float)prev[2];
+                    o3 += (float)prev[3];
+                }
                 const bf16x4_t o = {(__bf16)o0, (__bf16)o1, (__bf16)o2, (__bf16)o3};
-                *(bf16x4_t*)(og + (size_t)qi * D + d0) = o;
+                *dst = o;
             } else {
                 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+                f32x4_t* dst = (f32x4_t*)(og + (size_t)qi * D + d0);
+                if (sub) {
+                    const f32x4_t prev = *dst;
+                    o0 += prev[0];
+                    o1 += prev[1];
+                    o2 += prev[2];
+                    o3 += prev[3];
+                }
                 const f32x4_t o = {o0, o1, o2, o3};
-                *(f32x4_t*)(og + (size_t)qi * D + d0) = o;
+                *dst = o;
             }
         }
 }
@@ -858,16 +876,25 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
 
     const float lt = partner_sum(l_run);
     if (!wave_live || qi >= N) return;
-    const float inv = 1.f / lt;
+    const bool sub = p.lam != nullptr;  // differential attention: out -= lam * O/l
+    const float inv = (sub ? -p.lam[h] : 1.f) / lt;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int quad = 0; quad < 4; ++quad) {
             const int d0 = db * 32 + 8 * quad + 4 * g;
             typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-            const bf16x4_t o = {(__bf16)(oacc[db][4 * quad + 0] * inv), (__bf16)(oacc[db][4 * quad + 1] * inv),
-                                (__bf16)(oacc[db][4 * quad + 2] * inv), (__bf16)(oacc[db][4 * quad + 3] * inv)};
-            *(bf16x4_t*)(og + (size_t)qi * D + d0) = o;
+            bf16x4_t* dst = (bf16x4_t*)(og + (size_t)qi * D + d0);
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = oacc[db][4 * quad + e] * inv;
+            if (sub) {
+                const bf16x4_t prev = *dst;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] += (float)prev[e];
+            }
+            const bf16x4_t ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+            *dst = ob;
         }
 }
 

@@ -19,6 +19,7 @@ struct PrefillParams {
     const void* kring;     // chunk mode: [B, Hkv, W, d] history ring
     const void* vring;
     const int32_t* p0;     // chunk mode: [B] positions already cached
+    const float* lam;      // non-null: out -= lam[h] * result (second map of differential attention)
     int B, Hq, Hkv, N;
     int W;        // window (band modes: clamped to N; chunk mode: the ring size)
     int wr;       // two-sided band: keys up to i + wr are read too (0: causal)

@@ -117,3 +117,19 @@ def test_inputs_are_seeded_and_shaped():
     m = inputs.prefill_inputs(inputs.MISTRAL, N=64)
     # Q and K carry the 0.5 factor, V does not
     assert float(m[0].float().std()) < 0.7 and float(m[2].float().std()) > 0.8
+
+
+def test_two_sided_and_diff_reject_bad_arguments():
+    L = swa.lib()
+    base = (A, A * 2, A * 3, A * 1024, 1, 4, 2, 16, 64)
+    assert L.swa_attn_fwd_two_sided(*base, -1, 3, 0.125, None) == -1
+    assert L.swa_attn_fwd_two_sided(*base, 3, -2, 0.125, None) == -1
+    assert L.swa_attn_fwd_two_sided(A, A * 2, A * 3, A * 1024, 1, 4, 2, 16, 96, 3, 3, 0.125, None) == -2
+    assert L.swa_last_error().decode().startswith("swa_attn_fwd_two_sided")
+    # lam missing, misaligned; out overlapping q2; bad window
+    d = (A, A * 2, A * 3, A * 4, A * 5)
+    assert L.swa_diff_attn_fwd(*d, None, A * 1024, 1, 4, 2, 16, 64, 8, 0.125, None) == -1
+    assert L.swa_diff_attn_fwd(*d, A * 6 + 2, A * 1024, 1, 4, 2, 16, 64, 8, 0.125, None) == -1
+    assert L.swa_diff_attn_fwd(*d, A * 6, A * 3, 1, 4, 2, 16, 64, 8, 0.125, None) == -1
+    assert L.swa_diff_attn_fwd(*d, A * 6, A * 1024, 1, 4, 2, 16, 64, 0, 0.125, None) == -1
+    assert L.swa_last_error().decode().startswith("swa_diff_attn_fwd")
