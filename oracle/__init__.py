@@ -17,4 +17,6 @@ from .swa_oracle import (  # noqa: F401
     allowed_mask_two_sided,
     attn_fwd_two_sided,
     diff_attn_fwd,
+    allowed_mask_global,
+    attn_fwd_global,
 )

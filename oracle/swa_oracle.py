@@ -40,6 +40,13 @@ Everything here is the plain definition, written out in float64 with numpy:
   with a scalar lam per query head.  Here both maps use the same sliding-window
   band; with W >= N this is the page's causal version.
 
+* Local + global tokens (attention-variants page, 稀疏 / 块注意力, Longformer /
+  BigBird; SWA page, 其他 Sparse Attention 模式, Global Token): a few global
+  positions attend to every position and are attended to by every position,
+  the rest keep the local window.  In the causal setting of this library
+  "every position" means every position not after the row: row i may read
+  key j iff j <= i and (i - j < W or j is global or i is global).
+
 Readings where the pages leave a step open (each one is also listed in the
 design notes of the repository):
 
@@ -75,6 +82,8 @@ __all__ = [
     "allowed_mask_two_sided",
     "attn_fwd_two_sided",
     "diff_attn_fwd",
+    "allowed_mask_global",
+    "attn_fwd_global",
 ]
 
 
@@ -440,4 +449,50 @@ def diff_attn_fwd(q1, k1, q2, k2, v, lam, window: int, scale: Optional[float] = 
                 a2 = _masked_softmax_rows(scale * (np.asarray(q2[b, h, i0:i1 + 1], np.float64)
                                                    @ np.asarray(k2[b, g][keys], np.float64).T), allowed)
                 out[b, h, i0:i1 + 1] = (a1 - lam[h] * a2) @ np.asarray(v[b, g][keys], np.float64)
+    return out
+
+
+def allowed_mask_global(n: int, window: int, gidx) -> np.ndarray:
+    """Boolean n x n matrix of the causal local + global pattern: (i, j)
+    allowed iff j <= i and (i - j < W or j in gidx or i in gidx)."""
+    if window < 1:
+        raise ValueError("window must be >= 1")
+    glob = np.zeros(n, dtype=bool)
+    glob[np.asarray(list(gidx), dtype=np.int64)] = True
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    return (j <= i) & ((i - j < window) | glob[None, :] | glob[:, None])
+
+
+def attn_fwd_global(q, k, v, window: int, gidx, scale: Optional[float] = None) -> np.ndarray:
+    """Causal sliding window plus global positions gidx, float64
+    [B, Hq, N, d]: global rows read every earlier key, every row reads the
+    earlier global keys, other pairs follow the band."""
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, Hq, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or v.shape != k.shape or Hq % k.shape[1] != 0:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hq a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    g = np.asarray(sorted(set(int(x) for x in gidx)), dtype=np.int64)
+    glob = np.zeros(N, dtype=bool)
+    glob[g] = True
+    G = Hq // k.shape[1]
+    out = np.empty((B, Hq, N, v.shape[3]), dtype=np.float64)
+    block = 256
+    for b in range(B):
+        for h in range(Hq):
+            kk = np.asarray(k[b, h // G], dtype=np.float64)
+            vv = np.asarray(v[b, h // G], dtype=np.float64)
+            for i0 in range(0, N, block):
+                i1 = min(N, i0 + block) - 1
+                rows = np.arange(i0, i1 + 1)
+                keys = np.arange(0, i1 + 1)
+                i = rows[:, None]
+                j = keys[None, :]
+                allowed = (j <= i) & ((i - j < window) | glob[None, :i1 + 1] | glob[i0:i1 + 1, None])
+                scores = scale * (np.asarray(q[b, h, i0:i1 + 1], dtype=np.float64) @ kk[:i1 + 1].T)
+                out[b, h, i0:i1 + 1] = _masked_softmax_rows(scores, allowed) @ vv[:i1 + 1]
     return out

@@ -541,3 +541,59 @@ def test_diff_brute_force_page_causal_form():
         for c in range(d):
             want = sum((w1[j] / z1 - lam * w2[j] / z2) * v[j, c] for j in range(i + 1))
             assert abs(got[i, c] - want) <= 1e-12
+
+
+# ---------------------------------------------------------------- local + global tokens
+def _qkv(seed, B=1, Hq=4, Hkv=2, N=96, d=8):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, Hq, N, d)), rng.standard_normal((B, Hkv, N, d)),
+            rng.standard_normal((B, Hkv, N, d)))
+
+
+def test_global_with_no_global_positions_is_the_band():
+    q, k, v = _qkv(41)
+    assert np.abs(oracle.attn_fwd_global(q, k, v, 13, []) - oracle.attn_fwd(q, k, v, 13)).max() <= 1e-13
+
+
+def test_global_rows_are_full_causal_rows():
+    q, k, v = _qkv(42)
+    g = [0, 5, 50, 95]
+    got = oracle.attn_fwd_global(q, k, v, 7, g)
+    full = oracle.attn_fwd(q, k, v, 96)
+    assert np.abs(got[:, :, g] - full[:, :, g]).max() <= 1e-13
+
+
+def test_global_keys_on_a_stride_grid_match_the_strided_mask_on_other_rows():
+    """Global keys at 0, s, 2s, ... give non-global rows exactly the local +
+    strided pattern of the attention-variants page (its step 3)."""
+    q, k, v = _qkv(43, N=120)
+    s = 16
+    g = list(range(0, 120, s))
+    got = oracle.attn_fwd_global(q, k, v, 10, g)
+    strided = oracle.attn_fwd(q, k, v, 10, stride=s)
+    rows = [i for i in range(120) if i % s != 0]
+    assert np.abs(got[:, :, rows] - strided[:, :, rows]).max() <= 1e-13
+    m = oracle.allowed_mask_global(120, 10, g)
+    assert np.array_equal(m[rows], oracle.allowed_mask(120, 10, s)[rows])
+
+
+def test_global_everywhere_is_full_causal_sdpa():
+    q, k, v = _qkv(44, N=40)
+    got = oracle.attn_fwd_global(q, k, v, 3, range(40))
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(np.repeat(k, 2, axis=1)), torch.from_numpy(np.repeat(v, 2, axis=1)),
+        is_causal=True).numpy()
+    assert np.abs(got - want).max() <= 1e-12
+
+
+def test_global_sdpa_with_boolean_mask_and_brute_force():
+    q, k, v = _qkv(45, Hq=2, Hkv=2, N=70)
+    g = [3, 31, 32, 69]
+    m = torch.from_numpy(oracle.allowed_mask_global(70, 6, g))
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=m).numpy()
+    assert np.abs(oracle.attn_fwd_global(q, k, v, 6, g) - want).max() <= 1e-12
+    # the mask itself, pair by pair from the reading
+    for i in range(70):
+        for j in range(70):
+            assert m[i, j] == (j <= i and (i - j < 6 or j in g or i in g))
