@@ -154,6 +154,39 @@ SWA_API int swa_diff_attn_fwd_f32(const float* q1, const float* k1, const float*
                                   int window, float scale, hipStream_t stream);
 
 /*
+ * Causal local window plus global tokens (attention-variants page, 稀疏 /
+ * 块注意力, Longformer / BigBird; SWA page, 其他 Sparse Attention 模式,
+ * Global Token): a few global positions attend to every earlier position
+ * and every later position attends to them; the rest keep the window.  Row
+ * i reads key j iff j <= i and (i - j < window, or j is global, or i is
+ * global).
+ *   q, out : [B, Hq, N, d]   k, v : [B, Hkv, N, d]   (as swa_attn_fwd)
+ *   gidx   : int32 [ng] on the device, sorted ascending, distinct, each in
+ *            [0, N); the same positions for every sequence.  Not checked on
+ *            the device: unsorted or repeated entries give wrong results
+ *            (indices are clamped, so no out-of-bounds access).  ng = 0 is
+ *            the plain band.
+ *   workspace : device buffer of at least swa_attn_fwd_global_workspace_bytes
+ *            (may be NULL when that is 0), overwritten.
+ *   For ng > 0, Hq / Hkv must be 1, 2, 4 or 8 and B * ng <= 65535.
+ * Two kernels on `stream`: the band kernel with the global keys, then the
+ * split decode kernel over the global rows (their full causal rows, K/V
+ * read as a linear cache), which overwrites those rows of out.
+ */
+SWA_API int swa_attn_fwd_global(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N,
+                                int d, int window, const int32_t* gidx, int ng, float scale, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* Same contract with fp32 tensors and fp32 arithmetic. */
+SWA_API int swa_attn_fwd_global_f32(const float* q, const float* k, const float* v, float* out, int B, int Hq,
+                                    int Hkv, int N, int d, int window, const int32_t* gidx, int ng, float scale,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes swa_attn_fwd_global(_f32) needs (0 when ng == 0 or the
+ * global rows fit one split); 0 for invalid sizes. */
+SWA_API size_t swa_attn_fwd_global_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int ng);
+
+/*
  * Chunked prefill over the rolling cache (page "SWA：滑动窗口注意力与跨层信息传递",
  * §4.3): a chunk of T new tokens attends to the cached history plus its own
  * earlier rows, each row under its own band.  Chunk row r of sequence b is

@@ -36,6 +36,9 @@ SIGNATURES = {
     "swa_attn_fwd_two_sided_f32": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_diff_attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_diff_attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "swa_attn_fwd_global": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _F, _P, _Z, _P]),
+    "swa_attn_fwd_global_f32": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _F, _P, _Z, _P]),
+    "swa_attn_fwd_global_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
     "swa_chunk_prefill": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_chunk_prefill_f32": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_ring_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
@@ -189,6 +192,49 @@ def diff_attn_fwd(q1: torch.Tensor, k1: torch.Tensor, q2: torch.Tensor, k2: torc
     fn = lib().swa_diff_attn_fwd if dtype == torch.bfloat16 else lib().swa_diff_attn_fwd_f32
     _check(fn(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), v.data_ptr(), lam.data_ptr(),
               out.data_ptr(), B, Hq, k1.shape[1], N, d, int(window), float(scale), _stream(dev)))
+    return out
+
+
+def global_workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int, ng: int) -> int:
+    return int(lib().swa_attn_fwd_global_workspace_bytes(B, Hq, Hkv, N, d, ng))
+
+
+def attn_fwd_global(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: int, gidx: torch.Tensor,
+                    scale: float | None = None, out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal window plus global positions ``gidx`` (int32, sorted, distinct,
+    on the GPU).  Shapes as ``attn_fwd``."""
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q, k, v must be 4-D [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError("k, v do not match q")
+    dtype, dev = q.dtype, q.device
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bfloat16 or float32")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dtype, dev)
+    _need(gidx, "gidx", torch.int32, dev)
+    if gidx.dim() != 1:
+        raise ValueError("gidx must be 1-D")
+    ng = gidx.numel()
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype, dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    need = global_workspace_bytes(B, Hq, k.shape[1], N, d, ng)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = 0 if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    fn = lib().swa_attn_fwd_global if dtype == torch.bfloat16 else lib().swa_attn_fwd_global_f32
+    _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, k.shape[1], N, d, int(window),
+              gidx.data_ptr() if ng > 0 else None, ng, float(scale), ws_ptr or None, ws_bytes, _stream(dev)))
     return out
 
 

@@ -45,7 +45,7 @@ int check_scale(const char* name, float scale) {
 // min(N-1, i+right), plus the multiples of stride below the band.
 int band_fwd(bool bf16, const char* name, const void* q, const void* k, const void* v, void* out, int B, int Hq,
              int Hkv, int N, int d, int window, int right, int stride, float scale, hipStream_t stream,
-             const float* lam = nullptr) {
+             const float* lam = nullptr, const int32_t* gidx = nullptr, int ng = 0) {
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1)
         return fail(SWA_ERR_INVALID_ARG, "%s: B, N, Hq, Hkv must be >= 1 (B=%d N=%d Hq=%d Hkv=%d)", name, B, N, Hq,
                     Hkv);
@@ -69,7 +69,7 @@ int band_fwd(bool bf16, const char* name, const void* q, const void* k, const vo
     const long long rows = (long long)N * d;
     if ((long long)B * Hq * rows > (1ll << 40)) return fail(SWA_ERR_UNSUPPORTED, "%s: tensor too large", name);
 
-    swa::PrefillParams p;
+    swa::PrefillParams p{};
     p.q = q;
     p.k = k;
     p.v = v;
@@ -78,6 +78,8 @@ int band_fwd(bool bf16, const char* name, const void* q, const void* k, const vo
     p.vring = nullptr;
     p.p0 = nullptr;
     p.lam = lam;
+    p.gidx = gidx;
+    p.ng = ng;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
@@ -88,11 +90,12 @@ int band_fwd(bool bf16, const char* name, const void* q, const void* k, const vo
     p.c = fabsf(scale) * kLog2e;
     p.neg = scale < 0.f;
     p.G = (int)G;
-    swa::set_wave_split(p, swa::waves_per_group(bf16, p.stride > 0, p.G), N);
+    const int mode = ng > 0 ? swa::kGlobal : p.stride > 0 ? swa::kStrided : swa::kBand;
+    swa::set_wave_split(p, swa::waves_per_group(bf16, mode != swa::kBand, p.G), N);
     const long long total = (long long)B * Hkv * p.ngroups * p.nqb;
     if (total > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
     p.total = (int)total;
-    hipError_t e = swa::launch_band_fwd(bf16, d, p.stride > 0 ? swa::kStrided : swa::kBand, p, stream);
+    hipError_t e = swa::launch_band_fwd(bf16, d, mode, p, stream);
     if (e != hipSuccess) return fail(SWA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
     return ok();
 }
@@ -136,6 +139,68 @@ int diff_fwd(bool bf16, const void* q1, const void* k1, const void* q2, const vo
     return band_fwd(bf16, name, q2, k2, v, out, B, Hq, Hkv, N, d, window, 0, 0, scale, stream, lam);
 }
 
+size_t global_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int ng) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || ng < 1 || (long long)B * ng > 0x7fffffffll) return 0;
+    return swa::decode_workspace_bytes(B * ng, Hq, Hkv, N, d);
+}
+
+// Local + global tokens: the band kernel with the global keys (every row
+// reads the earlier global positions), then the global rows, which read
+// every earlier key, recomputed by the split decode kernel in row mode
+// over K/V as a linear cache of N slots; they overwrite the band result.
+int global_fwd(bool bf16, const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N,
+               int d, int window, const int32_t* gidx, int ng, float scale, void* workspace, size_t workspace_bytes,
+               hipStream_t stream) {
+    const char* name = bf16 ? "swa_attn_fwd_global" : "swa_attn_fwd_global_f32";
+    if (ng < 0 || (N >= 1 && ng > N))
+        return fail(SWA_ERR_INVALID_ARG, "%s: ng must be in 0..N (got %d)", name, ng);
+    if (ng > 0) {
+        if (gidx == nullptr || ((uintptr_t)gidx & 3u))
+            return fail(SWA_ERR_INVALID_ARG, "%s: gidx must be non-null, 4-byte aligned", name);
+        if (Hkv >= 1 && Hq % Hkv == 0) {
+            const int G = Hq / Hkv;
+            if (G != 1 && G != 2 && G != 4 && G != 8)
+                return fail(SWA_ERR_UNSUPPORTED, "%s: Hq/Hkv = %d not built for global rows (1, 2, 4 or 8)", name, G);
+        }
+        if ((long long)B * ng > 65535 || Hkv > 65535)
+            return fail(SWA_ERR_UNSUPPORTED, "%s: B * ng (%lld) too large", name, (long long)B * ng);
+        const size_t need = global_workspace_bytes(B, Hq, Hkv, N, d, ng);
+        if (need > 0 && !aligned16(workspace))
+            return fail(SWA_ERR_INVALID_ARG, "%s: workspace must be non-null and 16-byte aligned", name);
+        if (workspace_bytes < need)
+            return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes is below the %zu needed", name,
+                        workspace_bytes, need);
+    }
+    if (int rc = band_fwd(bf16, name, q, k, v, out, B, Hq, Hkv, N, d, window, 0, 0, scale, stream, nullptr,
+                          ng > 0 ? gidx : nullptr, ng))
+        return rc;
+    if (ng == 0) return ok();
+    swa::DecodeParams p{};
+    p.q = q;
+    p.kring = k;
+    p.vring = v;
+    p.pos = nullptr;
+    p.out = out;
+    p.B = B * ng;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.W = N;
+    p.gidx = gidx;
+    p.ng = ng;
+    p.N = N;
+    const swa::DecodeSplit plan = swa::decode_split_plan(p.B, Hkv, N);
+    p.split_len = plan.split_len;
+    p.nsplit = plan.nsplit;
+    p.ws_acc = (float*)workspace;
+    p.ws_ml = p.ws_acc + (size_t)p.B * Hq * p.nsplit * d;
+    p.c = fabsf(scale) * kLog2e;
+    p.neg = scale < 0.f;
+    if ((long long)p.nsplit > 65535) return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
+    hipError_t e = swa::launch_decode(bf16, d, Hq / Hkv, p, stream);
+    if (e != hipSuccess) return fail(SWA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
+    return ok();
+}
+
 int chunk_prefill(bool bf16, const void* q, const void* k, const void* v, const void* kring, const void* vring,
                   const int32_t* p0, void* out, int B, int Hq, int Hkv, int T, int d, int window, float scale,
                   hipStream_t stream) {
@@ -153,7 +218,7 @@ int chunk_prefill(bool bf16, const void* q, const void* k, const void* v, const 
     if (int rc = check_scale(name, scale)) return rc;
     if ((long long)T + window > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: T + window too large", name);
     const long long G = Hq / Hkv;
-    swa::PrefillParams p;
+    swa::PrefillParams p{};
     p.q = q;
     p.k = k;
     p.v = v;
@@ -220,7 +285,7 @@ int decode(bool bf16, const void* q, const void* kring, const void* vring, const
     if (workspace_bytes < need)
         return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes is below the %zu needed", name, workspace_bytes,
                     need);
-    swa::DecodeParams p;
+    swa::DecodeParams p{};
     p.q = q;
     p.kring = kring;
     p.vring = vring;
@@ -288,6 +353,24 @@ int swa_diff_attn_fwd_f32(const float* q1, const float* k1, const float* q2, con
                           const float* lam, float* out, int B, int Hq, int Hkv, int N, int d, int window, float scale,
                           hipStream_t stream) {
     return diff_fwd(false, q1, k1, q2, k2, v, lam, out, B, Hq, Hkv, N, d, window, scale, stream);
+}
+
+int swa_attn_fwd_global(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N, int d,
+                        int window, const int32_t* gidx, int ng, float scale, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    return global_fwd(true, q, k, v, out, B, Hq, Hkv, N, d, window, gidx, ng, scale, workspace, workspace_bytes,
+                      stream);
+}
+
+int swa_attn_fwd_global_f32(const float* q, const float* k, const float* v, float* out, int B, int Hq, int Hkv, int N,
+                            int d, int window, const int32_t* gidx, int ng, float scale, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    return global_fwd(false, q, k, v, out, B, Hq, Hkv, N, d, window, gidx, ng, scale, workspace, workspace_bytes,
+                      stream);
+}
+
+size_t swa_attn_fwd_global_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int ng) {
+    return global_workspace_bytes(B, Hq, Hkv, N, d, ng);
 }
 
 int swa_chunk_prefill(const void* q, const void* k, const void* v, const void* kring, const void* vring,

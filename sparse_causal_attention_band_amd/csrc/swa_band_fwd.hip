@@ -112,6 +112,8 @@ template <bool BF, int D, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) {
     constexpr bool STRIDED = MODE == kStrided;
     constexpr bool CHUNK = MODE == kChunk;
+    constexpr bool GLOBAL = MODE == kGlobal;
+    constexpr bool KEYLIST = STRIDED || GLOBAL;  // extra keys outside the window
     using elem_t = typename std::conditional<BF, uint16_t, float>::type;
     using frag_t = typename std::conditional<BF, bf16x8_t, float>::type;
     constexpr int RB = D * (int)sizeof(elem_t);      // bytes per K/V row
@@ -187,11 +189,24 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     const int kt_hi = min(NK - 1, qoff + q0 + BM - 1 + wr) / kTileN;
     const int kt_lo = max(0, qoff + q0 - W + 1) / kTileN;
     const int nband = kt_hi - kt_lo + 1;
+    // first entry of the sorted global list that is >= x (wave-uniform)
+    auto global_lb = [&](int x) __attribute__((always_inline)) {
+        int lo = 0, hi = p.ng;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (p.gidx[mid] < x)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        return lo;
+    };
+    // extra keys below the lowest band tile, read by every row: multiples of
+    // the stride, or the global positions there (a prefix of the sorted list)
     int M = 0, ncomp = 0;
-    if (STRIDED) {
-        M = (kt_lo * kTileN + p.stride - 1) / p.stride;
-        ncomp = (M + kTileN - 1) / kTileN;
-    }
+    if (STRIDED) M = (kt_lo * kTileN + p.stride - 1) / p.stride;
+    if (GLOBAL) M = global_lb(kt_lo * kTileN);
+    if (KEYLIST) ncomp = (M + kTileN - 1) / kTileN;
     const int ntiles = nband + ncomp;
 
     const bool wave_live = qw0 < N;  // some row of this wave is a real query
@@ -235,8 +250,10 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     auto issue_tile = [&](int t, char* kl, char* vl, bool do_k, bool do_v) __attribute__((always_inline)) {
         // key row behind tile row r (virtual index in chunk mode)
         auto key_of = [&](int r) __attribute__((always_inline)) {
-            return t < nband ? min((kt_hi - t) * kTileN + r, NK - 1)
-                             : min((t - nband) * kTileN + r, M - 1) * p.stride;
+            if (t < nband) return min((kt_hi - t) * kTileN + r, NK - 1);
+            const int m = min((t - nband) * kTileN + r, M - 1);
+            if constexpr (GLOBAL) return min(max(p.gidx[m], 0), NK - 1);
+            return m * p.stride;
         };
         // its row in HBM: the input, or in chunk mode the ring for history keys
         auto row_ptr = [&](const elem_t* in, const elem_t* ring, int j) __attribute__((always_inline)) {
@@ -317,6 +334,9 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
                 const int r0 = j0 % p.stride;
                 for (int o = r0 == 0 ? 0 : p.stride - r0; o < kTileN; o += p.stride) smask |= 1ull << o;
             }
+            if (GLOBAL && band) {
+                for (int e = global_lb(j0); e < p.ng && p.gidx[e] < j0 + kTileN; ++e) smask |= 1ull << (p.gidx[e] - j0);
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -328,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
                     // (keys past the end exist only as clamped copies of
                     // the last row; causal rows never reach them)
                     const bool in_band = (dist >= -wr) & (j0 + r < NK) &
-                                         ((dist < W) | (STRIDED & (((smask >> r) & 1ull) != 0)));
+                                         ((dist < W) | (KEYLIST & (((smask >> r) & 1ull) != 0)));
                     const bool in_comp = (t - nband) * kTileN + r < M;
                     sc[kb][i] = (band ? in_band : in_comp) ? sc[kb][i] : -INFINITY;
                 }
@@ -900,7 +920,7 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
 
 template <bool BF, int D, int MODE>
 hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
-    if constexpr (BF && MODE != kStrided) {
+    if constexpr (BF && (MODE == kBand || MODE == kChunk)) {
         if (p.HG * p.PB == 8) {
             hipLaunchKernelGGL((band8_kernel<D, MODE>), dim3(p.total), dim3(kThreads8), 0, s, p);
             return hipGetLastError();
@@ -914,6 +934,7 @@ template <bool BF, int D>
 hipError_t launch_mode(int mode, const PrefillParams& p, hipStream_t s) {
     if (mode == kStrided) return launch_one<BF, D, kStrided>(p, s);
     if (mode == kChunk) return launch_one<BF, D, kChunk>(p, s);
+    if (mode == kGlobal) return launch_one<BF, D, kGlobal>(p, s);
     return launch_one<BF, D, kBand>(p, s);
 }
 

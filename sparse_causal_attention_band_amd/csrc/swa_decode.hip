@@ -72,7 +72,33 @@ __device__ __forceinline__ float wave_max(float x) {
     return x;
 }
 
-template <bool BF, int D, int G>
+// Where entry e reads its query rows and writes its output rows: element
+// offset of head 0 and the stride between heads; its KV sequence and the
+// number of positions it has (decode: pos[e]; row mode: row gidx + 1).
+struct EntryRows {
+    size_t row0, head_stride;
+    int seq, pos;
+};
+template <bool GR, int D>
+__device__ __forceinline__ EntryRows entry_rows(const DecodeParams& p, int e) {
+    EntryRows r;
+    if constexpr (GR) {
+        const int b = e / p.ng;
+        const int i = min(max(p.gidx[e % p.ng], 0), p.N - 1);
+        r.seq = b;
+        r.pos = i + 1;
+        r.row0 = ((size_t)b * p.Hq * p.N + i) * D;
+        r.head_stride = (size_t)p.N * D;
+    } else {
+        r.seq = e;
+        r.pos = p.pos[e];
+        r.row0 = (size_t)e * p.Hq * D;
+        r.head_stride = D;
+    }
+    return r;
+}
+
+template <bool BF, int D, int G, bool GR>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams p) {
     using elem_t = typename std::conditional<BF, uint16_t, float>::type;
     constexpr int ES = (int)sizeof(elem_t);
@@ -91,9 +117,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
 
     const int tid = threadIdx.x;
     const int dc = tid % CPR, rg = tid / CPR;
-    const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int split = blockIdx.x, kvh = blockIdx.y;
+    const EntryRows er = entry_rows<GR, D>(p, blockIdx.z);
+    const int b = er.seq;
     const int W = p.W;
-    const int pb = p.pos[b];
+    const int pb = er.pos;
     const int n = pb <= 0 ? 0 : min(pb, W);
     const int s0 = split * p.split_len;
     const int s1 = min(n, s0 + p.split_len);
@@ -102,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
         // merge (one split) this is a pos <= 0 row, which is all zeros
         if (p.nsplit == 1)
             for (int u = tid; u < G * D; u += kThreads)
-                ((elem_t*)p.out)[(size_t)(b * p.Hq + kvh * G + u / D) * D + u % D] = (elem_t)0;
+                ((elem_t*)p.out)[er.row0 + (size_t)(kvh * G + u / D) * er.head_stride + u % D] = (elem_t)0;
         return;
     }
 
@@ -115,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     u32x4_t qc[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-        u32x4_t w = *(const u32x4_t*)((const char*)p.q + ((size_t)(b * p.Hq + h0 + hh) * D) * ES + dc * 16);
+        u32x4_t w = *(const u32x4_t*)((const char*)p.q + (er.row0 + (size_t)(h0 + hh) * er.head_stride) * ES + dc * 16);
         if (p.neg) w ^= (BF ? 0x80008000u : 0x80000000u);
         qc[hh] = w;
     }
@@ -282,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
                 const float m = sm_ml[r][hh][0];
                 if (m != -INFINITY) L += sm_ml[r][hh][1] * __builtin_amdgcn_exp2f(m - M);
             }
-            elem_t* out = (elem_t*)p.out + (size_t)(b * p.Hq + h0 + hh) * D + d;
+            elem_t* out = (elem_t*)p.out + er.row0 + (size_t)(h0 + hh) * er.head_stride + d;
             if constexpr (BF) {
                 const __bf16 x = (__bf16)(a / L);
                 *out = __builtin_bit_cast(uint16_t, x);
@@ -292,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
         }
         return;
     }
-    const size_t part = ((size_t)(b * p.Hq + h0) * p.nsplit + split);  // head hh adds hh * nsplit
+    const size_t part = ((size_t)(blockIdx.z * p.Hq + h0) * p.nsplit + split);  // head hh adds hh * nsplit
     for (int u = tid; u < G * D; u += kThreads) {
         const int hh = u / D, d = u % D;
         float a = 0.f;
@@ -315,13 +343,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
 }
 
 // Merge the splits of one (sequence, query head): weights 2^(m_s - M).
-template <bool BF, int D>
+template <bool BF, int D, bool GR>
 __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
     using elem_t = typename std::conditional<BF, uint16_t, float>::type;
     const int bh = blockIdx.x;
-    const int b = bh / p.Hq;
+    const EntryRows er = entry_rows<GR, D>(p, bh / p.Hq);
     const int d = threadIdx.x;
-    const int pb = p.pos[b];
+    const int pb = er.pos;
     const int n = pb <= 0 ? 0 : min(pb, p.W);
     const int ns = (n + p.split_len - 1) / p.split_len;
     const float* ml = p.ws_ml + (size_t)bh * p.nsplit * 2;
@@ -336,7 +364,7 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
     }
     const float r = (ns > 0) ? o / L : 0.f;
     if (d < D) {
-        elem_t* out = (elem_t*)p.out + (size_t)bh * D + d;
+        elem_t* out = (elem_t*)p.out + er.row0 + (size_t)(bh % p.Hq) * er.head_stride + d;
         if constexpr (BF) {
             const __bf16 x = (__bf16)r;
             *out = __builtin_bit_cast(uint16_t, x);
@@ -346,13 +374,18 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
     }
 }
 
-template <bool BF, int D, int G>
-hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((decode_split_kernel<BF, D, G>), dim3(p.nsplit, p.Hkv, p.B), dim3(kThreads), 0, s, p);
+template <bool BF, int D, int G, bool GR>
+hipError_t launch_gr(const DecodeParams& p, hipStream_t s) {
+    hipLaunchKernelGGL((decode_split_kernel<BF, D, G, GR>), dim3(p.nsplit, p.Hkv, p.B), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<BF, D>), dim3(p.B * p.Hq), dim3(128), 0, s, p);
+    hipLaunchKernelGGL((decode_merge_kernel<BF, D, GR>), dim3(p.B * p.Hq), dim3(128), 0, s, p);
     return hipGetLastError();
+}
+
+template <bool BF, int D, int G>
+hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
+    return p.gidx ? launch_gr<BF, D, G, true>(p, s) : launch_gr<BF, D, G, false>(p, s);
 }
 
 template <bool BF, int D>

@@ -9,7 +9,7 @@
 namespace swa {
 
 // ---------------------------------------------------------------- prefill
-enum { kBand = 0, kStrided = 1, kChunk = 2 };
+enum { kBand = 0, kStrided = 1, kChunk = 2, kGlobal = 3 };
 
 struct PrefillParams {
     const void* q;
@@ -20,6 +20,8 @@ struct PrefillParams {
     const void* vring;
     const int32_t* p0;     // chunk mode: [B] positions already cached
     const float* lam;      // non-null: out -= lam[h] * result (second map of differential attention)
+    const int32_t* gidx;   // global mode: sorted global positions [ng]
+    int ng;
     int B, Hq, Hkv, N;
     int W;        // window (band modes: clamped to N; chunk mode: the ring size)
     int wr;       // two-sided band: keys up to i + wr are read too (0: causal)
@@ -48,8 +50,9 @@ constexpr int kKeysPerTile = 64;
 // Waves per workgroup of the band kernels.  Every wave of a workgroup walks
 // the key tiles of all its rows, so a workgroup should span few positions:
 // bf16 band and chunk modes with at least four query heads per KV head run
-// 8 waves (4 heads x 64 positions), everything else 4 waves.
-inline int waves_per_group(bool bf16, bool strided, int G) { return bf16 && !strided && G % 4 == 0 ? 8 : 4; }
+// 8 waves (4 heads x 64 positions), everything else (fp32, and the modes
+// with extra keys outside the window) 4 waves.
+inline int waves_per_group(bool bf16, bool keylist, int G) { return bf16 && !keylist && G % 4 == 0 ? 8 : 4; }
 
 // Split a workgroup's waves into HG query heads (of one KV head) times PB
 // blocks of 32 positions: HG is the largest power of two <= waves dividing G.
@@ -74,6 +77,12 @@ struct DecodeParams {
     float* ws_ml;    // [B, Hq, nsplit, 2]  (running max in log2 units, sum)
     int B, Hq, Hkv, W;
     int nsplit;      // ceil(W / split_len); 1 = the split kernel writes out itself
+    // Row mode (global rows of the local + global pattern): entry e of the
+    // B entries is sequence e / ng, row i = gidx[e % ng] of q/out laid out
+    // [B/ng, Hq, N, d]; it reads keys 0..i of kring/vring = K/V [B/ng, Hkv, N, d]
+    // (W = N).  nullptr: ordinary decode entries.
+    const int32_t* gidx;
+    int ng, N;
     int split_len;   // ring slots per split (multiple of the 64-slot tile)
     float c;         // |scale| * log2(e)
     int neg;

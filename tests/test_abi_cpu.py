@@ -133,3 +133,22 @@ def test_two_sided_and_diff_reject_bad_arguments():
     assert L.swa_diff_attn_fwd(*d, A * 6, A * 3, 1, 4, 2, 16, 64, 8, 0.125, None) == -1
     assert L.swa_diff_attn_fwd(*d, A * 6, A * 1024, 1, 4, 2, 16, 64, 0, 0.125, None) == -1
     assert L.swa_last_error().decode().startswith("swa_diff_attn_fwd")
+
+
+def test_global_rejects_bad_arguments_and_sizes_its_workspace():
+    L = swa.lib()
+    args = lambda **kw: [kw.get(n, dflt) for n, dflt in (
+        ("q", A), ("k", A * 2), ("v", A * 3), ("out", A * 1024), ("B", 1), ("Hq", 8), ("Hkv", 2), ("N", 4096),
+        ("d", 128), ("window", 64), ("gidx", A * 5), ("ng", 4), ("scale", 0.1), ("ws", A * 6),
+        ("wsb", 1 << 30), ("stream", None))]
+    assert L.swa_attn_fwd_global(*args(gidx=None)) == -1
+    assert L.swa_attn_fwd_global(*args(gidx=A * 5 + 2)) == -1
+    assert L.swa_attn_fwd_global(*args(ng=-1)) == -1
+    assert L.swa_attn_fwd_global(*args(ng=5000)) == -1            # more global positions than N
+    assert L.swa_attn_fwd_global(*args(Hq=6, Hkv=2)) == -2        # 3 heads per KV head: no row kernel
+    assert L.swa_attn_fwd_global(*args(wsb=16)) == -1
+    assert L.swa_last_error().decode().startswith("swa_attn_fwd_global")
+    # one (sequence, global row) entry per decode entry: 4 rows x 2 KV heads
+    # -> 64 splits of 64-key tiles over N = 4096 keys, d + 2 floats each
+    assert L.swa_attn_fwd_global_workspace_bytes(1, 8, 2, 4096, 128, 4) == 4 * 8 * 64 * 130 * 4
+    assert L.swa_attn_fwd_global_workspace_bytes(1, 8, 2, 4096, 128, 0) == 0
