@@ -16,9 +16,11 @@ counts against the kernel).  The same line carries:
   * chunk      -- chunked prefill over the rolling cache (4 sequences x 4096
                   new tokens, cached lengths 0 / 1500 / 4095 / 61440) in
                   in-band TFLOP/s, and the ring append of the same chunk;
-  * cpu_baseline -- the float64 oracle on the host cores over a bounded
-                  sample of the same workload (run before the GPU is touched,
-                  since its worker pool forks).
+  * variants   -- the same layer under the two-sided band, differential
+                  attention and global-token masks (in-band TFLOP/s);
+  * cpu_baseline -- the float64 oracle on the host cores over the whole
+                  prefill workload (run before the GPU is touched, since its
+                  worker pool forks).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -37,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "band_fwd_traffic_mistral.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "band8_traffic_mistral16k.txt")
 BAND_SOURCES = ["sparse_causal_attention_band_amd/csrc/swa_band_fwd.hip",
                 "sparse_causal_attention_band_amd/csrc/swa_internal.h",
                 "sparse_causal_attention_band_amd/build.py"]
@@ -115,6 +117,63 @@ def decode_cpu_baseline(cfg, q, kr, vr, pos):
     return dt
 
 
+def two_sided_pairs(N: int, left: int, right: int) -> int:
+    """sum_i |S_i| of the two-sided band: min(i, left) + min(N-1-i, right) + 1."""
+    return sum(min(i, left) + min(N - 1 - i, right) + 1 for i in range(N))
+
+
+def global_pairs(N: int, W: int, g) -> int:
+    """sum_i |S_i| of the causal window plus global positions g: a global row
+    reads i + 1 keys, another row its min(i+1, W) band keys plus the global
+    positions below its band."""
+    gs = sorted(set(g))
+    gset = set(gs)
+    total = 0
+    below = 0  # global positions < i - W + 1 (the band start)
+    for i in range(N):
+        while below < len(gs) and gs[below] < i - W + 1:
+            below += 1
+        total += (i + 1) if i in gset else min(i + 1, W) + below
+    return total
+
+
+def variant_legs(swa, inputs, torch, dev, args):
+    """The Mistral-shaped layer (B=1, 32/8 heads, d=128, N=16384, bf16) under
+    the other masks: two-sided band (left = right = 2048, the [i - W/2,
+    i + W/2] window with W = 4096), differential attention (two maps, W =
+    4096, lam per head in [0.5, 0.8]) and W = 4096 plus 16 global positions
+    (0 and every 1024th).  In-band TFLOP/s counts only allowed pairs."""
+    cfg = inputs.MISTRAL
+    q, k, v = (x.to(dev) for x in inputs.prefill_inputs(cfg))
+    B, Hq, Hkv, N, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d
+    steps, warm = max(5, args.steps // 3), 2
+    res = {}
+
+    def leg(name, fn, pairs_per_head, maps=1, extra=None):
+        per, _ = time_launches(lambda i=0: fn(), steps, warm, torch)
+        ms = sum(per) / len(per)
+        fl = 4.0 * B * Hq * d * pairs_per_head * maps
+        res[name] = {"value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                     "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "avg_ms": round(ms, 4), "algorithmic_flops": fl}
+        if extra:
+            res[name].update(extra)
+
+    out = torch.empty_like(q)
+    leg("two_sided_l2048_r2048", lambda: swa.attn_fwd_two_sided(q, k, v, 2048, 2048, out=out),
+        two_sided_pairs(N, 2048, 2048))
+    q2, k2 = q.flip(2).contiguous(), k.flip(2).contiguous()
+    lam = torch.linspace(0.5, 0.8, Hq, device=dev)
+    leg("diff_w4096", lambda: swa.diff_attn_fwd(q, k, q2, k2, v, lam, 4096, out=out),
+        allowed_pairs(N, 4096, 0), maps=2)
+    g = [0] + list(range(1024, N, 1024))
+    gi = torch.tensor(g, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, swa.global_workspace_bytes(B, Hq, Hkv, N, d, len(g))), dtype=torch.uint8, device=dev)
+    leg("global_w4096_g16", lambda: swa.attn_fwd_global(q, k, v, 4096, gi, out=out, workspace=ws),
+        global_pairs(N, 4096, g), extra={"global_positions": len(g)})
+    return res
+
+
 def time_launches(fn, steps, warmup, torch):
     for _ in range(warmup):
         fn()
@@ -135,12 +194,15 @@ def time_launches(fn, steps, warmup, torch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    # the warm-up also brings the GPU clock up after the host-side baseline
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="mistral", choices=["mistral", "gemma", "strided"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the two-sided, differential and global-token legs")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -167,7 +229,7 @@ def main():
     cpu = None
     dec_cpu_s = None
     if not args.no_cpu_baseline:
-        rows = list(range(cfg.N - 4096, cfg.N))
+        rows = list(range(cfg.N))  # the whole workload: every row of every (batch, head)
         cpu = cpu_baseline(cfg, q, k, v, rows)
         if not args.no_decode:
             dec_cpu_s = decode_cpu_baseline(dcfg, dq, dkr, dvr, dpos)
@@ -186,7 +248,8 @@ def main():
     traffic = read_traffic(cfg.name)
     roof = {"bound": "mfma", "achieved": round(value, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-            "kernel": "band_fwd_kernel<bf16, d=128>", "avg_launch_ms": round(ms, 4),
+            "kernel": "band8_kernel<d=128, band>" if cfg.Hq // cfg.Hkv % 4 == 0 and cfg.stride == 0
+            else "band_fwd_kernel<bf16, d=%d>" % cfg.d, "avg_launch_ms": round(ms, 4),
             "algorithmic_flops_per_launch": flops}
 
     line = {
@@ -258,10 +321,13 @@ def main():
         line["chunk"] = {"workload": ccfg.name, "p0": list(ccfg.p0), "value": round(cflops / (cms * 1e-3) / 1e12, 2),
                          "unit": "TFLOP/s", "frac_mfma": round(cflops / (cms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                          "avg_launch_ms": round(cms, 4), "algorithmic_flops_per_launch": cflops,
-                         "kernel": "band_fwd_kernel<bf16, d=128, chunk>",
+                         "kernel": "band8_kernel<d=128, chunk>",
                          "ring_append": {"avg_launch_ms": round(ams, 4), "bytes": abytes,
                                          "GB_s": round(abytes / (ams * 1e-3) / 1e9, 1)}}
         del cq, ck, cv, ckr, cvr, cp0, cout
+
+    if not args.no_variants:
+        line["variants"] = variant_legs(swa, inputs, torch, dev, args)
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
