@@ -1,0 +1,124 @@
+"""Degenerate and boundary cases of every entry point, against the float64
+oracle: one-token sequences, window 1, one global position, one-token chunks
+over empty and very long histories, positions near the int32 limit, grids
+with many sequences, and the head groupings the 8-wave kernel takes."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_causal_attention_band_amd as swa
+from sparse_causal_attention_band_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    swa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def f64(t):
+    return t.detach().cpu().double().numpy()
+
+
+def check(got, want, dtype, what=""):
+    g = f64(got)
+    err = np.abs(g - want)
+    assert np.isfinite(g).all(), what
+    if dtype == torch.float32:
+        assert err.max() <= 1e-5, f"{what}: max err {err.max():.3e}"
+    else:
+        assert err.max() <= 1.5e-2 and err.mean() <= 1e-3, f"{what}: max {err.max():.3e} mean {err.mean():.3e}"
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_one_token_sequences(dt):
+    say(f"N=1 everywhere {dt}")
+    q, k, v = inputs.random_qkv(3, 8, 2, 1, 128, dt, seed=51)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    outs = {
+        "band": swa.attn_fwd(qd, kd, vd, window=7),
+        "strided": swa.attn_fwd(qd, kd, vd, window=1, stride=3),
+        "two_sided": swa.attn_fwd_two_sided(qd, kd, vd, 5, 5),
+        "global": swa.attn_fwd_global(qd, kd, vd, 4, torch.zeros(1, dtype=torch.int32, device=DEV)),
+        "diff": swa.diff_attn_fwd(qd, kd, qd, kd, vd, torch.full((8,), 0.5, device=DEV), 3),
+    }
+    torch.cuda.synchronize()
+    # a single key: every variant returns V (the difference (1 - lam) V)
+    want = np.repeat(f64(v), 4, axis=1)
+    for name, o in outs.items():
+        w = 0.5 * want if name == "diff" else want
+        check(o, w, dt, name)
+
+
+def test_many_sequences_and_the_8_wave_grouping():
+    """B = 24 sequences, 16 query heads over 2 KV heads (8 per group: the
+    8-wave kernel with 8 heads and one position block), ragged N."""
+    say("B=24 G=8 ragged")
+    q, k, v = inputs.random_qkv(24, 16, 2, 77, 64, torch.bfloat16, seed=52)
+    out = swa.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), window=20)
+    torch.cuda.synchronize()
+    check(out, oracle.attn_fwd(f64(q), f64(k), f64(v), 20), torch.bfloat16, "B=24")
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_chunk_edges(dt):
+    """One-token chunks with window 1 and window larger than the history,
+    over an empty history and over one near the int32 limit."""
+    say(f"chunk edges {dt}")
+    B, Hq, Hkv, d = 3, 4, 2, 64
+    for W, p0s in ((1, [0, 5, 2 ** 31 - 10]), (50, [0, 49, 2 ** 31 - 100])):
+        g = torch.Generator().manual_seed(W)
+        q = torch.randn(B, Hq, 1, d, generator=g).to(dt)
+        k = torch.randn(B, Hkv, 1, d, generator=g).to(dt)
+        v = torch.randn(B, Hkv, 1, d, generator=g).to(dt)
+        kr = torch.randn(B, Hkv, W, d, generator=g).to(dt)
+        vr = torch.randn(B, Hkv, W, d, generator=g).to(dt)
+        p0 = torch.tensor(p0s, dtype=torch.int32)
+        out = swa.chunk_prefill(q.to(DEV), k.to(DEV), v.to(DEV), kr.to(DEV), vr.to(DEV), p0.to(DEV))
+        krd, vrd = kr.to(DEV), vr.to(DEV)
+        swa.ring_append(k.to(DEV), v.to(DEV), p0.to(DEV), krd, vrd)
+        torch.cuda.synchronize()
+        want = oracle.chunk_prefill(f64(q), f64(k), f64(v), f64(kr), f64(vr), p0s, W, 1 / math.sqrt(d))
+        check(out, want, dt, f"W={W}")
+        wk, wv = oracle.ring_append(f64(kr), f64(vr), f64(k), f64(v), p0s, W)
+        assert np.array_equal(f64(krd), wk) and np.array_equal(f64(vrd), wv)
+
+
+def test_decode_position_near_the_int32_limit():
+    say("decode pos near 2^31")
+    B, Hq, Hkv, d, W = 2, 8, 2, 128, 96
+    g = torch.Generator().manual_seed(53)
+    q = torch.randn(B, Hq, d, generator=g).to(torch.bfloat16)
+    kr = torch.randn(B, Hkv, W, d, generator=g).to(torch.bfloat16)
+    vr = torch.randn(B, Hkv, W, d, generator=g).to(torch.bfloat16)
+    pos = torch.tensor([2 ** 31 - 1, 2 ** 31 - 97], dtype=torch.int32)
+    out = swa.decode(q.to(DEV), kr.to(DEV), vr.to(DEV), pos.to(DEV))
+    torch.cuda.synchronize()
+    check(out, oracle.decode(f64(q), f64(kr), f64(vr), pos.numpy().astype(np.int64), W, 1 / math.sqrt(d)),
+          torch.bfloat16, "pos")
+
+
+def test_global_all_positions_and_last_position():
+    say("global: every position, and only the last one")
+    q, k, v = inputs.random_qkv(2, 4, 2, 70, 64, torch.float32, seed=54)
+    for g in (list(range(70)), [69]):
+        gi = torch.tensor(g, dtype=torch.int32, device=DEV)
+        out = swa.attn_fwd_global(q.to(DEV), k.to(DEV), v.to(DEV), 5, gi)
+        torch.cuda.synchronize()
+        check(out, oracle.attn_fwd_global(f64(q), f64(k), f64(v), 5, g), torch.float32, f"ng={len(g)}")
