@@ -534,8 +534,21 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
 //    K(t+3) and V(t+2), and waits only for the copies issued one step earlier;
 //  * this tile's probabilities, its P*V product and the next tile's scores
 //    form one straight-line block, 16 keys at a time, so that every matrix
-//    instruction has vector work of the same wave beside it.
+//    instruction has vector work of the same wave beside it.  The K fragments
+//    of each 16-key region are read from LDS one region ahead, and the
+//    region's V fragments before its score instructions;
+//  * the copies are buffer loads into LDS rather than global-segment loads:
+//    the latter are FLAT instructions that may also address LDS, and with
+//    one in flight the compiler's wait counting can no longer wait for a
+//    single LDS read (every wait in the loop became a full drain).
 constexpr int kThreads8 = 512;
+
+// Raw buffer resource over [base, base + bytes): stride 0, bounds checked
+// per access (out of range reads return zero).  bytes < 2^31 (checked on
+// the host).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 __device__ __forceinline__ void lds_barrier() {
     // this wave's LDS reads done, then the workgroup barrier: no fence, so
@@ -579,7 +592,8 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     const int N = p.N;
     int qoff = 0, hslot0 = 0;
     if constexpr (CHUNK) {
-        const int start = max(p.p0[b], 0);
+        // uniform per workgroup: scalar registers, so the copy offsets stay scalar
+        const int start = __builtin_amdgcn_readfirstlane(max(p.p0[b], 0));
         qoff = min(start, p.W - 1);
         hslot0 = (start - qoff) % p.W;
     }
@@ -604,6 +618,11 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     const elem_t* vrg = CHUNK ? (const elem_t*)p.vring + ring_head : nullptr;
 
     const int wr = p.wr;  // right radius of a two-sided band (0: causal)
+    // every kernel argument the epilogue needs is in registers before the
+    // tile loop: a scalar load still in flight there would force every LDS
+    // wait in the loop to drain all outstanding reads
+    const float* lam_ptr = p.lam;
+    asm volatile("" ::"s"(lam_ptr));
     const int kt_hi = min(NK - 1, qoff + q0 + BM - 1 + wr) / kTileN;
     const int kt_lo = max(0, qoff + q0 - W + 1) / kTileN;
     const int nband = kt_hi - kt_lo + 1;
@@ -643,18 +662,6 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     auto key_of = [&](int t, int r) __attribute__((always_inline)) {
         return t < nband ? min((kt_hi - t) * kTileN + r, NK - 1) : min((t - nband) * kTileN + r, M - 1) * p.stride;
     };
-    auto row_ptr = [&](const elem_t* in, const elem_t* ring, int j) __attribute__((always_inline)) {
-        if constexpr (CHUNK) {
-            if (j < qoff) {
-                int slot = hslot0 + j;
-                slot -= slot >= p.W ? p.W : 0;
-                return ring + (size_t)slot * D;
-            }
-            return in + (size_t)(j - qoff) * D;
-        } else {
-            return in + (size_t)j * D;
-        }
-    };
     // copies: wave w fills 1 KiB blocks w, w+8, ... of the tile (lane i
     // writes bytes 16i..16i+15 of a block).  Per block the lane's source is
     // a fixed byte offset inside the tile's 64 rows (K: row sigma(pos),
@@ -672,52 +679,77 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         const int vr = P / RB;
         voff[it] = (uint32_t)(vr * RB + ((P % RB) ^ vswz(vr)));
     }
-    // first row of tile t in the virtual sequence, and whether its 64 rows
-    // are consecutive rows of one array (the returned base)
-    auto tile_base = [&](int t, const elem_t* in, const elem_t* ring, const char*& base) __attribute__((always_inline)) {
-        if (t >= nband) return false;
+    // The copies are buffer loads straight into LDS (MUBUF "lds" form).  A
+    // resource covers one (sequence, KV head) array; the byte offset of a
+    // row is a lane offset, plus a scalar tile offset when the tile's 64 rows
+    // are consecutive rows of one array.  (The global-segment form of the
+    // same copy is a FLAT instruction that may touch LDS, which makes every
+    // later LDS or memory wait in the loop drain completely.)
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg, (size_t)N * RB);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg, (size_t)N * RB);
+    const __amdgpu_buffer_rsrc_t rkr = CHUNK ? make_rsrc(krg, (size_t)p.W * RB) : rk;
+    const __amdgpu_buffer_rsrc_t rvr = CHUNK ? make_rsrc(vrg, (size_t)p.W * RB) : rv;
+    // tile t's rows as one run: 0 = gathered rows, 1 = input array at byte
+    // offset soff, 2 = ring at soff
+    auto tile_run = [&](int t, int& soff) __attribute__((always_inline)) {
+        if (t >= nband) return 0;
         const int j0 = (kt_hi - t) * kTileN;
-        if (j0 + kTileN > NK) return false;
+        if (j0 + kTileN > NK) return 0;
         if constexpr (CHUNK) {
             if (j0 >= qoff) {
-                base = (const char*)(in + (size_t)(j0 - qoff) * D);
-                return true;
+                soff = (j0 - qoff) * RB;
+                return 1;
             }
             if (j0 + kTileN <= qoff && hslot0 + j0 + kTileN <= p.W) {
-                base = (const char*)(ring + (size_t)(hslot0 + j0) * D);
-                return true;
+                soff = (hslot0 + j0) * RB;
+                return 2;
             }
-            return false;
+            return 0;
         } else {
-            base = (const char*)(in + (size_t)j0 * D);
-            return true;
+            soff = j0 * RB;
+            return 1;
         }
     };
-    // The empty asm statements in the two paths differ, which keeps the
-    // compiler from merging their last loads into one flat-address load.
-    auto issue_rows = [&](int t, char* dst, const elem_t* in, const elem_t* ring, const uint32_t* off)
-        __attribute__((always_inline)) {
-        const char* base;
-        if (!STRIDED && tile_base(t, in, ring, base)) {
+    auto issue_rows = [&](int t, char* dst, __amdgpu_buffer_rsrc_t rin, __amdgpu_buffer_rsrc_t rring,
+                          const uint32_t* off) __attribute__((always_inline)) {
+        int soff = 0;
+        const int run = STRIDED ? 0 : tile_run(t, soff);
+        if (run != 0) {
+            const __amdgpu_buffer_rsrc_t r = run == 1 ? rin : rring;
 #pragma unroll
             for (int it = 0; it < NBLK; ++it)
-                __builtin_amdgcn_global_load_lds(base + off[it],
-                                                 (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024),
-                                                 16, 0, 0);
-            asm volatile("; tile copy: contiguous rows" ::: "memory");
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    r, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024), 16, (int)off[it], soff, 0, 0);
         } else {
 #pragma unroll
             for (int it = 0; it < NBLK; ++it) {
                 const int row = (int)(off[it] / RB);
-                const char* src = (const char*)row_ptr(in, ring, key_of(t, row)) + (off[it] % RB);
-                __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024),
-                                                 16, 0, 0);
+                const int byte = (int)(off[it] % RB);
+                const int j = key_of(t, row);
+                auto* l = (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024);
+                if constexpr (CHUNK) {
+                    // history rows come from the ring, the rest from the chunk
+                    // (lanes on either side load under their own mask: never
+                    // fewer loads than the fixed wait count assumes)
+                    // (the two empty asm statements differ, so that the compiler
+                    // cannot merge the loads into one with a per-lane resource)
+                    if (j < qoff) {
+                        int slot = hslot0 + j;
+                        slot -= slot >= p.W ? p.W : 0;
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rring, l, 16, slot * RB + byte, 0, 0, 0);
+                        asm volatile("; ring rows" ::: "memory");
+                    } else {
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rin, l, 16, (j - qoff) * RB + byte, 0, 0, 0);
+                        asm volatile("; chunk rows" ::: "memory");
+                    }
+                } else {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rin, l, 16, j * RB + byte, 0, 0, 0);
+                }
             }
-            asm volatile("; tile copy: gathered rows" ::: "memory");
         }
     };
-    auto issue_k = [&](int t, char* kl) __attribute__((always_inline)) { issue_rows(t, kl, kg, krg, koff); };
-    auto issue_v = [&](int t, char* vl) __attribute__((always_inline)) { issue_rows(t, vl, vg, vrg, voff); };
+    auto issue_k = [&](int t, char* kl) __attribute__((always_inline)) { issue_rows(t, kl, rk, rkr, koff); };
+    auto issue_v = [&](int t, char* vl) __attribute__((always_inline)) { issue_rows(t, vl, rv, rvr, voff); };
     // Every step issues the same copies (past the end of the list the last
     // tile again, into a buffer nobody reads any more), so one fixed wait
     // count holds: the 2*NBLK loads of the current step may stay in flight.
@@ -750,23 +782,38 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         const bool edge = band ? !(j0 + kTileN - 1 <= qvw0 + wr && j0 >= qvw0 + kQw - W && j0 + kTileN <= NK)
                                : ((t - nband + 1) * kTileN > M);
         if (edge) {
-            uint64_t smask = 0;
-            if (STRIDED && band) {
-                const int r0 = j0 % p.stride;
-                for (int o = r0 == 0 ? 0 : p.stride - r0; o < kTileN; o += p.stride) smask |= 1ull << o;
+            // key of element i in block kb is j0 + 8g + C, C = kb*32 + 16*(i/8) + i%8;
+            // with x = qv - j0 - 8g its distance is x - C, so each test is one
+            // compare of a per-tile bound against a constant (the empty asm
+            // keeps the compiler from turning them into 32 loop-invariant
+            // per-lane constants)
+            int lo, hi, nk;
+            uint64_t sm = 0;
+            if (band) {
+                const int x = qv - j0 - 8 * g;
+                lo = x + wr;              // dist >= -wr  <=>  C <= lo
+                hi = x - W;               // dist < W     <=>  C > hi
+                nk = NK - j0 - 8 * g;     // key < NK     <=>  C < nk
+                if (STRIDED) {
+                    const int r0 = j0 % p.stride;
+                    uint64_t smask = 0;
+                    for (int o = r0 == 0 ? 0 : p.stride - r0; o < kTileN; o += p.stride) smask |= 1ull << o;
+                    sm = smask >> (8 * g);
+                }
+            } else {
+                lo = kTileN;
+                hi = kTileN;
+                nk = M - (t - nband) * kTileN - 8 * g;  // compact entry < M
             }
+            asm volatile("" : "+v"(lo), "+v"(hi), "+v"(nk));
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int r = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
-                    const int dist = qv - (j0 + r);
-                    // (keys past the end exist only as clamped copies of
-                    // the last row; causal rows never reach them)
-                    const bool in_band = (dist >= -wr) & (j0 + r < NK) &
-                                         ((dist < W) | (STRIDED & (((smask >> r) & 1ull) != 0)));
-                    const bool in_comp = (t - nband) * kTileN + r < M;
-                    sc[kb][i] = (band ? in_band : in_comp) ? sc[kb][i] : -INFINITY;
+                    const int C = kb * 32 + 16 * (i >> 3) + (i & 7);
+                    const bool keep = band ? (C <= lo) & (C < nk) & ((C > hi) | (STRIDED & (((sm >> C) & 1ull) != 0)))
+                                           : (C < nk);
+                    sc[kb][i] = keep ? sc[kb][i] : -INFINITY;
                 }
         }
     };
@@ -792,8 +839,20 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     // probabilities, row sum and P*V (from sc, vl); DO_S = the next tile's
     // scores (into sn, from kl).  16 keys at a time, so that every matrix
     // instruction has vector work of the same wave beside it.
-    auto tile_work = [&](auto do_pv, auto do_s, f32x16_t* sc, f32x16_t* sn, const char* kl, const char* vl)
-        __attribute__((always_inline)) {
+    // K fragments of one 16-key region of the score block (the
+    // contraction chunks cc = c2 * NQF/4 ..), loaded one region ahead
+    struct KFrag {
+        bf16x8_t a[NQF / 2];
+    };
+    auto load_k = [&](const char* kl, int c2, KFrag& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NQF / 2; ++i) {
+            const int kb = i & 1, cc = c2 * (NQF / 4) + (i >> 1);
+            f.a[i] = *(const bf16x8_t*)(kl + k_lane + ((kb * 2 * CPR + 2 * cc) << 8));
+        }
+    };
+    auto tile_work = [&](auto do_pv, auto do_s, f32x16_t* sc, f32x16_t* sn, const char* kl, const char* vl,
+                         KFrag& kf0) __attribute__((always_inline)) {
         constexpr bool DP = decltype(do_pv)::value, DS = decltype(do_s)::value;
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -819,23 +878,30 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             pb[c2] = __builtin_bit_cast(bf16x8_t, pw);
             asm volatile("" : "+v"(rsv[c2]));  // keep the dot chain beside its exponentials
         };
-        auto mfmas = [&](int c2) __attribute__((always_inline)) {
+        KFrag kf1;
+        auto mfmas = [&](int c2, const KFrag& kf) __attribute__((always_inline)) {
+            u32x4_t vf[NDB];
+            if constexpr (DP) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const char* vp = vl + v_lane + ((64 * db) ^ vq) + 16 * c2 * RB;
+                    const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lds_read_tr16(vp));
+                    const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, lds_read_tr16(vp + 4 * RB));
+                    vf[db] = u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
+                }
+            }
+            if constexpr (DS) {
+                if (c2 < 3) load_k(kl, c2 + 1, (c2 & 1) ? kf0 : kf1);
+            }
 #pragma unroll
             for (int i = 0; i < NQF / 2; ++i) {
                 if constexpr (DS) {
                     const int kb = i & 1, cc = c2 * (NQF / 4) + (i >> 1);
-                    const bf16x8_t a = *(const bf16x8_t*)(kl + k_lane + ((kb * 2 * CPR + 2 * cc) << 8));
-                    sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], sn[kb], 0, 0, 0);
+                    sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.a[i], qf[cc], sn[kb], 0, 0, 0);
                 }
                 if constexpr (DP) {
                     const int db = i;
-                    const char* vp = vl + v_lane + ((64 * db) ^ vq) + 16 * c2 * RB;
-                    const i16x4_t lo = lds_read_tr16(vp);
-                    const i16x4_t hi = lds_read_tr16(vp + 4 * RB);
-                    const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
-                    const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
-                    const u32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a4), pb[c2],
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[db]), pb[c2],
                                                                       oacc[db], 0, 0, 0);
                 }
             }
@@ -844,7 +910,7 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
 #pragma unroll
         for (int c2 = 0; c2 < 4; ++c2) {
             __builtin_amdgcn_sched_barrier(0);
-            mfmas(c2);
+            mfmas(c2, (c2 & 1) ? kf1 : kf0);
             if constexpr (DP) {
                 if (c2 < 3) probs(c2 + 1);
             }
@@ -873,10 +939,12 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     auto step = [&](int t, const char* kn, const char* vc, char* ki, char* vi) __attribute__((always_inline)) {
         issue_k(min(t + 3, n - 1), ki);
         issue_v(min(t + 2, n - 1), vi);
+        KFrag kf0;
+        load_k(kn, 0, kf0);
         softmax_head(scur);
         f32x16_t snext[2];
         // past the last tile the score block reads stale data and is discarded
-        tile_work(std::true_type{}, std::true_type{}, scur, snext, kn, vc);
+        tile_work(std::true_type{}, std::true_type{}, scur, snext, kn, vc, kf0);
         if (t + 1 < n) mask_tile(t + 1, snext);
         scur[0] = snext[0];
         scur[1] = snext[1];
@@ -921,7 +989,9 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
 template <bool BF, int D, int MODE>
 hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
     if constexpr (BF && (MODE == kBand || MODE == kChunk)) {
-        if (p.HG * p.PB == 8) {
+        // (the 8-wave kernel addresses a K/V array with 32-bit byte offsets)
+        const size_t rows = (size_t)(MODE == kChunk ? max(p.N, p.W) : p.N);
+        if (p.HG * p.PB == 8 && rows * D * 2 < (size_t(1) << 31)) {
             hipLaunchKernelGGL((band8_kernel<D, MODE>), dim3(p.total), dim3(kThreads8), 0, s, p);
             return hipGetLastError();
         }
