@@ -24,7 +24,7 @@
 //  * Key tiles of 64 rows are visited from the diagonal tile down to the
 //    lowest tile that meets the band; with stride > 0 a compact list of the
 //    strided keys below the band follows (rows gathered at j = m * stride).
-//    Each tile is copied HBM -> LDS directly (global_load_lds, 16 bytes per
+//    Each tile is copied HBM -> LDS directly (a 16-byte buffer load per
 //    lane, coalesced), double-buffered, one barrier per tile.
 //  * Per wave the score block is computed transposed, S^T = K Q^T, with the
 //    32x32 matrix-core instruction (bf16: 32x32x16, fp32: 32x32x2).  In that
@@ -106,6 +106,12 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
         (__attribute__((address_space(3))) i16x4_t*)(p));
 }
 
+// Buffer resource over `rows` rows of `row_bytes` bytes (structured: a load
+// names a row and a byte inside it; rows >= `rows` read as zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int row_bytes, int rows) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)row_bytes, rows, 0x00020000);
+}
+
 // MODE: kBand (window only), kStrided (window + multiples of the stride),
 // kChunk (a chunk of new queries over the ring history plus the chunk).
 template <bool BF, int D, int MODE>
@@ -139,7 +145,8 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     __shared__ __attribute__((aligned(16))) char vb1[VTILE_BYTES];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS copy targets stay scalar
     const int g = lane >> 5, l32 = lane & 31;
 
     // ---- which workgroup tile is this
@@ -159,7 +166,8 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     // other modes qoff = 0 and the virtual sequence is the input.
     int qoff = 0, hslot0 = 0;
     if constexpr (CHUNK) {
-        const int start = max(p.p0[b], 0);
+        // uniform per workgroup: scalar registers, so the copy offsets stay scalar
+        const int start = __builtin_amdgcn_readfirstlane(max(p.p0[b], 0));
         qoff = min(start, p.W - 1);
         hslot0 = (start - qoff) % p.W;  // ring slot of the oldest history position used
     }
@@ -242,11 +250,19 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     const int v_lane = BF ? ((8 * g + ((lane & 15) >> 2)) * RBV + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2)
                           : (8 * g * RBV + l32 * 4);
 
-    // ---- tile copy HBM -> LDS without registers: each wave's
-    // global_load_lds_dwordx4 fills one contiguous 1 KiB block of LDS (lane i
-    // writes bytes 16i..16i+15 of it), so the layout is applied by choosing
-    // which global 16-byte chunk each lane fetches.  Rows past the end are clamped to a valid row: those keys are
-    // always masked, and the copy never leaves non-finite bits in LDS.
+    // ---- tile copy HBM -> LDS without registers: each wave's 16-byte
+    // buffer load with the "lds" flag fills one contiguous 1 KiB block of LDS
+    // (lane i writes bytes 16i..16i+15 of it), so the layout is applied by
+    // choosing which 16-byte chunk of which row each lane fetches.  Rows past
+    // the end are clamped to a valid row: those keys are always masked, and
+    // the copy never leaves non-finite bits in LDS.  The resources address
+    // (row, byte in row) of one (sequence, KV head) array; buffer loads,
+    // unlike the global-segment form of the copy, are not FLAT instructions,
+    // so the compiler can still wait for single LDS reads while copies fly.
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kg, RB, N);
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vg, RB, N);
+    const __amdgpu_buffer_rsrc_t rkr = CHUNK ? rows_rsrc(krg, RB, p.W) : rk;
+    const __amdgpu_buffer_rsrc_t rvr = CHUNK ? rows_rsrc(vrg, RB, p.W) : rv;
     auto issue_tile = [&](int t, char* kl, char* vl, bool do_k, bool do_v) __attribute__((always_inline)) {
         // key row behind tile row r (virtual index in chunk mode)
         auto key_of = [&](int r) __attribute__((always_inline)) {
@@ -255,17 +271,25 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
             if constexpr (GLOBAL) return min(max(p.gidx[m], 0), NK - 1);
             return m * p.stride;
         };
-        // its row in HBM: the input, or in chunk mode the ring for history keys
-        auto row_ptr = [&](const elem_t* in, const elem_t* ring, int j) __attribute__((always_inline)) {
+        // copy 16 bytes of key row j into LDS: from the input, or in chunk
+        // mode from the ring for history keys (the two empty asm statements
+        // differ, so the compiler cannot merge the two loads into one with a
+        // per-lane resource)
+        auto copy16 = [&](__amdgpu_buffer_rsrc_t in, __amdgpu_buffer_rsrc_t ring, int j, int byte, char* dst)
+            __attribute__((always_inline)) {
+            auto* l = (__attribute__((address_space(3))) void*)dst;
             if constexpr (CHUNK) {
                 if (j < qoff) {
                     int slot = hslot0 + j;
                     slot -= slot >= p.W ? p.W : 0;
-                    return ring + (size_t)slot * D;
+                    __builtin_amdgcn_struct_ptr_buffer_load_lds(ring, l, 16, slot, byte, 0, 0, 0);
+                    asm volatile("; ring rows" ::: "memory");
+                } else {
+                    __builtin_amdgcn_struct_ptr_buffer_load_lds(in, l, 16, j - qoff, byte, 0, 0, 0);
+                    asm volatile("; chunk rows" ::: "memory");
                 }
-                return in + (size_t)(j - qoff) * D;
             } else {
-                return in + (size_t)j * D;
+                __builtin_amdgcn_struct_ptr_buffer_load_lds(in, l, 16, j, byte, 0, 0, 0);
             }
         };
 #pragma unroll
@@ -276,8 +300,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
             const int within = P % (CPR * 256);
             const int pos = (P / (CPR * 256)) * 16 + ((within >> 4) & 15);
             const int ch = within >> 8;
-            const char* src = (const char*)row_ptr(kg, krg, key_of(sigma(pos))) + (ch << 4);
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(kl + blk), 16, 0, 0);
+            copy16(rk, rkr, key_of(sigma(pos)), ch << 4, kl + blk);
         }
 #pragma unroll
         for (int it = 0; it < NCHV; ++it) {
@@ -285,10 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
             const int blk = (wave * NCHV + it) * 1024;
             const int P = blk + lane * 16;
             const int row = P / RBV, inrow = P % RBV;
-            if (inrow < RB) {
-                const char* src = (const char*)row_ptr(vg, vrg, key_of(row)) + inrow;
-                __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(vl + blk), 16, 0, 0);
-            }
+            if (inrow < RB) copy16(rv, rvr, key_of(row), inrow, vl + blk);
         }
     };
 
