@@ -699,6 +699,14 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         const int vr = P / RB;
         voff[it] = (uint32_t)(vr * RB + ((P % RB) ^ vswz(vr)));
     }
+    // band mode: byte offset of the last key row plus the lane's byte in a row
+    // (the clamp of a copy's row to NK - 1, see issue_rows)
+    uint32_t klim[NBLK], vlim[NBLK];
+#pragma unroll
+    for (int it = 0; it < NBLK; ++it) {
+        klim[it] = (uint32_t)((NK - 1) * RB) + koff[it] % RB;
+        vlim[it] = (uint32_t)((NK - 1) * RB) + voff[it] % RB;
+    }
     // The copies are buffer loads straight into LDS (MUBUF "lds" form).  A
     // resource covers one (sequence, KV head) array; the byte offset of a
     // row is a lane offset, plus a scalar tile offset when the tile's 64 rows
@@ -731,7 +739,23 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         }
     };
     auto issue_rows = [&](int t, char* dst, __amdgpu_buffer_rsrc_t rin, __amdgpu_buffer_rsrc_t rring,
-                          const uint32_t* off) __attribute__((always_inline)) {
+                          const uint32_t* off, const uint32_t* lim) __attribute__((always_inline)) {
+        if constexpr (!CHUNK) {
+            // Band mode: one copy instruction per block whatever the tile (a
+            // branch between a contiguous and a gathered copy leaves the
+            // compiler's copy tracking unsure at the join, and it then drains
+            // all copies before the next LDS read).  Row j0 + r clamped to
+            // NK - 1 is, in bytes, min(j0*RB + off, (NK-1)*RB + byte): the
+            // clamp is monotonic in the row and the byte within the row is
+            // the lane's own.
+            const uint32_t base = (uint32_t)((kt_hi - t) * kTileN * RB);
+#pragma unroll
+            for (int it = 0; it < NBLK; ++it)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rin, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024), 16,
+                    (int)min(base + off[it], lim[it]), 0, 0, 0);
+            return;
+        }
         int soff = 0;
         const int run = STRIDED ? 0 : tile_run(t, soff);
         if (run != 0) {
@@ -768,8 +792,8 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             }
         }
     };
-    auto issue_k = [&](int t, char* kl) __attribute__((always_inline)) { issue_rows(t, kl, rk, rkr, koff); };
-    auto issue_v = [&](int t, char* vl) __attribute__((always_inline)) { issue_rows(t, vl, rv, rvr, voff); };
+    auto issue_k = [&](int t, char* kl) __attribute__((always_inline)) { issue_rows(t, kl, rk, rkr, koff, klim); };
+    auto issue_v = [&](int t, char* vl) __attribute__((always_inline)) { issue_rows(t, vl, rv, rvr, voff, vlim); };
     // Every step issues the same copies (past the end of the list the last
     // tile again, into a buffer nobody reads any more), so one fixed wait
     // count holds: the 2*NBLK loads of the current step may stay in flight.
