@@ -357,20 +357,36 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
             if (GLOBAL && band) {
                 for (int e = global_lb(j0); e < p.ng && p.gidx[e] < j0 + kTileN; ++e) smask |= 1ull << (p.gidx[e] - j0);
             }
+            // Element i of block kb holds key j0 + 8g + C with the constant
+            // C = kb*32 + 16*(i/8) + i%8; with x = qv - j0 - 8g its distance is
+            // x - C, so each test compares one per-tile bound with a constant
+            // (the empty asm keeps the compiler from hoisting 32 per-lane key
+            // offsets out of the tile loop instead).
+            int lo, hi, nk;
+            if (band) {
+                const int x = qv - j0 - 8 * g;
+                lo = x + wr;           // dist >= -wr  <=>  C <= lo
+                hi = x - W;            // dist < W     <=>  C > hi
+                nk = NK - j0 - 8 * g;  // key < NK     <=>  C < nk
+            } else {
+                lo = kTileN;
+                hi = kTileN;
+                nk = M - (t - nband) * kTileN - 8 * g;  // compact entry < M
+            }
+            asm volatile("" : "+v"(lo), "+v"(hi), "+v"(nk));
+            const uint64_t sm = smask >> (8 * g);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     // non-short-circuit operators: a straight-line select,
                     // no per-element divergent branches
-                    const int r = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
-                    const int dist = qv - (j0 + r);
+                    const int C = kb * 32 + 16 * (i >> 3) + (i & 7);
                     // (keys past the end exist only as clamped copies of
                     // the last row; causal rows never reach them)
-                    const bool in_band = (dist >= -wr) & (j0 + r < NK) &
-                                         ((dist < W) | (KEYLIST & (((smask >> r) & 1ull) != 0)));
-                    const bool in_comp = (t - nband) * kTileN + r < M;
-                    sc[kb][i] = (band ? in_band : in_comp) ? sc[kb][i] : -INFINITY;
+                    const bool keep = band ? (C <= lo) & (C < nk) & ((C > hi) | (KEYLIST & (((sm >> C) & 1ull) != 0)))
+                                           : (C < nk);
+                    sc[kb][i] = keep ? sc[kb][i] : -INFINITY;
                 }
         }
     };
