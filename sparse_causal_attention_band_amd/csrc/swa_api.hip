@@ -91,7 +91,7 @@ int band_fwd(bool bf16, const char* name, const void* q, const void* k, const vo
     p.neg = scale < 0.f;
     p.G = (int)G;
     const int mode = ng > 0 ? swa::kGlobal : p.stride > 0 ? swa::kStrided : swa::kBand;
-    swa::set_wave_split(p, swa::waves_per_group(bf16, mode != swa::kBand, p.G), N);
+    swa::set_wave_split(p, swa::waves_per_group(bf16, mode != swa::kBand, p.G, N, d), N);
     const long long total = (long long)B * Hkv * p.ngroups * p.nqb;
     if (total > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
     p.total = (int)total;
@@ -237,7 +237,7 @@ int chunk_prefill(bool bf16, const void* q, const void* k, const void* v, const 
     p.c = fabsf(scale) * kLog2e;
     p.neg = scale < 0.f;
     p.G = (int)G;
-    swa::set_wave_split(p, swa::waves_per_group(bf16, false, p.G), T);
+    swa::set_wave_split(p, swa::waves_per_group(bf16, false, p.G, T > window ? T : window, d), T);
     const long long total = (long long)B * Hkv * p.ngroups * p.nqb;
     if (total > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
     p.total = (int)total;

@@ -1049,9 +1049,9 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
 template <bool BF, int D, int MODE>
 hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
     if constexpr (BF && (MODE == kBand || MODE == kChunk)) {
-        // (the 8-wave kernel addresses a K/V array with 32-bit byte offsets)
-        const size_t rows = (size_t)(MODE == kChunk ? max(p.N, p.W) : p.N);
-        if (p.HG * p.PB == 8 && rows * D * 2 < (size_t(1) << 31)) {
+        // (the host picks 8 waves only where the 8-wave kernel applies,
+        // including its 32-bit byte offsets into a K/V array)
+        if (p.HG * p.PB == 8) {
             hipLaunchKernelGGL((band8_kernel<D, MODE>), dim3(p.total), dim3(kThreads8), 0, s, p);
             return hipGetLastError();
         }

@@ -122,3 +122,45 @@ def test_global_all_positions_and_last_position():
         out = swa.attn_fwd_global(q.to(DEV), k.to(DEV), v.to(DEV), 5, gi)
         torch.cuda.synchronize()
         check(out, oracle.attn_fwd_global(f64(q), f64(k), f64(v), 5, g), torch.float32, f"ng={len(g)}")
+
+
+def test_key_value_arrays_beyond_2_gib():
+    """K and V of one head just past 2 GiB each (N = 2^23 + 100 rows of d=128
+    bf16): the 8-wave kernel addresses an array with 32-bit byte offsets, so
+    such shapes run on the 4-wave kernel, whose copies address rows by index.
+    Sampled rows, the last ones beyond the 2 GiB offset included, against the
+    oracle evaluated on each row's own key range; the same rows as a first
+    chunk of a chunked prefill (no history, NaN ring) too."""
+    N, d, W, Hq = 2 ** 23 + 100, 128, 64, 4
+    say(f"N={N} Hq={Hq} Hkv=1 d={d} W={W} bf16 (~20 GiB on the device)")
+    g = torch.Generator(device=DEV).manual_seed(55)
+    q = torch.randn(1, Hq, N, d, generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn(1, 1, N, d, generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn(1, 1, N, d, generator=g, device=DEV).to(torch.bfloat16)
+    assert k[0, 0].numel() * 2 >= 2 ** 31
+    out = swa.attn_fwd(q, k, v, window=W)
+    # the same rows as a first chunk (no history): chunk mode on the same path
+    kr = torch.full((1, 1, W, d), float("nan"), device=DEV).to(torch.bfloat16)
+    vr = torch.full((1, 1, W, d), float("nan"), device=DEV).to(torch.bfloat16)
+    outc = swa.chunk_prefill(q, k, v, kr, vr, torch.zeros(1, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    rows = [0, 1, 63, 64, 5000, 2 ** 22, 2 ** 23 - 1, 2 ** 23, 2 ** 23 + 37, N - 65, N - 2, N - 1]
+    got, gotc, want = [], [], []
+    for idx, i in enumerate(rows):
+        h = idx % Hq
+        lo = max(0, i - W + 1)
+        qs = q[:, h:h + 1, i:i + 1].cpu().float().numpy()
+        ks = k[:, :, lo:i + 1].cpu().float().numpy()
+        vs = v[:, :, lo:i + 1].cpu().float().numpy()
+        # the row's band is the whole slice: place the query at its last
+        # position of a slice-length sequence
+        L = i + 1 - lo
+        qpad = np.zeros((1, 1, L, d))
+        qpad[:, :, L - 1] = qs[:, :, 0]
+        want.append(oracle.attn_fwd_rows(qpad, ks, vs, W, 0, 1 / math.sqrt(d), [(0, 0, L - 1)])[0])
+        got.append(out[0, h, i].float().cpu())
+        gotc.append(outc[0, h, i].float().cpu())
+    del q, k, v, out, outc
+    torch.cuda.empty_cache()
+    check(torch.stack(got), np.stack(want), torch.bfloat16, "beyond 2 GiB")
+    check(torch.stack(gotc), np.stack(want), torch.bfloat16, "beyond 2 GiB, chunk")
