@@ -375,19 +375,32 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
             }
             asm volatile("" : "+v"(lo), "+v"(hi), "+v"(nk));
             const uint64_t sm = smask >> (8 * g);
+            // which bounds this tile can violate (wave-uniform): most edge
+            // tiles need one compare per element, not three
+            const bool need_lo = j0 + kTileN - 1 > qvw0 + wr, need_nk = j0 + kTileN > NK;
+            const bool need_hi = j0 < qvw0 + kQw - W;
+            auto apply = [&](auto keep_of) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    // non-short-circuit operators: a straight-line select,
-                    // no per-element divergent branches
-                    const int C = kb * 32 + 16 * (i >> 3) + (i & 7);
-                    // (keys past the end exist only as clamped copies of
-                    // the last row; causal rows never reach them)
-                    const bool keep = band ? (C <= lo) & (C < nk) & ((C > hi) | (KEYLIST & (((sm >> C) & 1ull) != 0)))
-                                           : (C < nk);
-                    sc[kb][i] = keep ? sc[kb][i] : -INFINITY;
-                }
+                    for (int i = 0; i < 16; ++i) {
+                        const int C = kb * 32 + 16 * (i >> 3) + (i & 7);
+                        sc[kb][i] = keep_of(C) ? sc[kb][i] : -INFINITY;
+                    }
+            };
+            if (!KEYLIST && band && !need_hi && !need_nk) {
+                apply([&](int C) { return C <= lo; });
+            } else if (!KEYLIST && band && !need_lo && !need_nk) {
+                apply([&](int C) { return C > hi; });
+            } else {
+                // non-short-circuit operators: a straight-line select, no
+                // per-element divergent branches.  (Keys past the end exist
+                // only as clamped copies of the last row; causal rows never
+                // reach them.)
+                apply([&](int C) {
+                    return band ? (C <= lo) & (C < nk) & ((C > hi) | (KEYLIST & (((sm >> C) & 1ull) != 0))) : (C < nk);
+                });
+            }
         }
     };
 
@@ -866,15 +879,28 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
                 nk = M - (t - nband) * kTileN - 8 * g;  // compact entry < M
             }
             asm volatile("" : "+v"(lo), "+v"(hi), "+v"(nk));
+            // which bounds this tile can violate (wave-uniform): most edge
+            // tiles need one compare per element, not three
+            const bool need_lo = j0 + kTileN - 1 > qvw0 + wr, need_nk = j0 + kTileN > NK;
+            const bool need_hi = j0 < qvw0 + kQw - W;
+            auto apply = [&](auto keep_of) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int C = kb * 32 + 16 * (i >> 3) + (i & 7);
-                    const bool keep = band ? (C <= lo) & (C < nk) & ((C > hi) | (STRIDED & (((sm >> C) & 1ull) != 0)))
-                                           : (C < nk);
-                    sc[kb][i] = keep ? sc[kb][i] : -INFINITY;
-                }
+                    for (int i = 0; i < 16; ++i) {
+                        const int C = kb * 32 + 16 * (i >> 3) + (i & 7);
+                        sc[kb][i] = keep_of(C) ? sc[kb][i] : -INFINITY;
+                    }
+            };
+            if (!STRIDED && band && !need_hi && !need_nk) {
+                apply([&](int C) { return C <= lo; });
+            } else if (!STRIDED && band && !need_lo && !need_nk) {
+                apply([&](int C) { return C > hi; });
+            } else {
+                apply([&](int C) {
+                    return band ? (C <= lo) & (C < nk) & ((C > hi) | (STRIDED & (((sm >> C) & 1ull) != 0))) : (C < nk);
+                });
+            }
         }
     };
     auto softmax_head = [&](f32x16_t* sc) __attribute__((always_inline)) {
