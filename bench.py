@@ -31,6 +31,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -56,11 +57,22 @@ def allowed_pairs(N: int, W: int, stride: int) -> int:
     return total
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments, whitespace collapsed: a comment edit
+    leaves the compiled kernel, and so its measured traffic, unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return " ".join(text.split())
+
+
 def band_source_hash() -> str:
     h = hashlib.sha256()
     for rel in BAND_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        if rel.endswith((".hip", ".h")):
+            text = _code_only(text)
+        h.update(text.encode("utf-8"))
     return h.hexdigest()[:16]
 
 
