@@ -14,11 +14,13 @@
 // that KV head, so every K/V byte is read from HBM once.  With one split
 // (512 or more (sequence, KV head) pairs) the workgroup writes the output
 // itself.  The kernel is a pure register stream:
-//   * a 16-byte chunk per lane, a ring row of d elements spread over CPR
-//     consecutive lanes (one 256-byte bf16 row per 16 lanes: every load
-//     instruction reads 1 KiB of contiguous HBM), a 3-deep ring of tiles in
-//     registers so two more tiles are in flight while one is consumed; the
-//     loads are non-temporal (each byte is read once per step);
+//   * 16-byte chunks per lane, a ring row of d elements spread over CPR
+//     consecutive lanes: a 256-byte bf16 row over 8 lanes with two chunks
+//     each (chunks c and c + 8, so every load instruction reads whole
+//     128-byte lines) where up to four query heads share the KV head, else
+//     one chunk per lane; a 3-deep ring of tiles in registers so two more
+//     tiles are in flight while one is consumed; the loads are non-temporal
+//     (each byte is read once per step);
 //   * scores: per-lane partial dot products (v_dot2 on bf16 pairs), summed
 //     over the lanes of a row with DPP row permutes;
 //   * each group of lanes sharing a row keeps its own online softmax (max,
@@ -103,7 +105,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     using elem_t = typename std::conditional<BF, uint16_t, float>::type;
     constexpr int ES = (int)sizeof(elem_t);
     constexpr int RB = D * ES;          // bytes per ring row
-    constexpr int CPR = RB / 16;        // lanes per row (one 16-byte chunk each)
+    // 16-byte chunks per lane: two for bf16 rows of 128 with up to four heads
+    // per KV head (a row over 8 lanes: half the cross-lane sums and
+    // exponentials per lane), else one
+    constexpr int CW = (BF && D == 128 && G <= 4) ? 2 : 1;
+    constexpr int CPR = RB / (16 * CW);  // lanes per row
     constexpr int EPC = 16 / ES;        // elements per chunk
     constexpr int RG = kThreads / CPR;  // row groups per workgroup
     constexpr int RPT = kTile / RG;     // rows per lane per tile
@@ -139,43 +145,51 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     const char* vg = (const char*)((const elem_t*)p.vring + ring) + dc * 16;
     const int h0 = kvh * G;
 
-    // this lane's 16-byte chunk of every query row (sign of the scale folded in)
-    u32x4_t qc[G];
+    // this lane's 16-byte chunks (dc, dc + CPR, ...) of every query row (sign
+    // of the scale folded in)
+    u32x4_t qc[G][CW];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        u32x4_t w = *(const u32x4_t*)((const char*)p.q + (er.row0 + (size_t)(h0 + hh) * er.head_stride) * ES + dc * 16);
-        if (p.neg) w ^= (BF ? 0x80008000u : 0x80000000u);
-        qc[hh] = w;
-    }
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int c = 0; c < CW; ++c) {
+            u32x4_t w = *(const u32x4_t*)((const char*)p.q + (er.row0 + (size_t)(h0 + hh) * er.head_stride) * ES +
+                                          (dc + c * CPR) * 16);
+            if (p.neg) w ^= (BF ? 0x80008000u : 0x80000000u);
+            qc[hh][c] = w;
+        }
 
     const int ntile = (s1 - s0 + kTile - 1) / kTile;
-    u32x4_t kr[PD][RPT], vr[PD][RPT];
-    auto load = [&](int t, u32x4_t* kd, u32x4_t* vd) __attribute__((always_inline)) {
+    u32x4_t kr[PD][RPT][CW], vr[PD][RPT][CW];
+    auto load = [&](int t, u32x4_t (*kd)[CW], u32x4_t (*vd)[CW]) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < RPT; ++k) {
             const int slot = s0 + t * kTile + rg + RG * k;
-            u32x4_t kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-            if (t < ntile && slot < s1) {
-                // read once per step: non-temporal loads stream past the caches
-                kw = __builtin_nontemporal_load((const u32x4_t*)(kg + (size_t)slot * RB));
-                vw = __builtin_nontemporal_load((const u32x4_t*)(vg + (size_t)slot * RB));
+            const bool live = t < ntile && slot < s1;
+#pragma unroll
+            for (int c = 0; c < CW; ++c) {
+                u32x4_t kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
+                if (live) {
+                    // read once per step: non-temporal loads stream past the caches
+                    kw = __builtin_nontemporal_load((const u32x4_t*)(kg + (size_t)slot * RB + c * CPR * 16));
+                    vw = __builtin_nontemporal_load((const u32x4_t*)(vg + (size_t)slot * RB + c * CPR * 16));
+                }
+                kd[k][c] = kw;
+                vd[k][c] = vw;
             }
-            kd[k] = kw;
-            vd[k] = vw;
         }
     };
 
-    float m_h[G], l_h[G], acc[G][EPC];
+    float m_h[G], l_h[G], acc[G][EPC * CW];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
         m_h[hh] = -INFINITY;
         l_h[hh] = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[hh][e] = 0.f;
+        for (int e = 0; e < EPC * CW; ++e) acc[hh][e] = 0.f;
     }
     const float c = p.c;
 
-    auto consume = [&](int t, const u32x4_t* kd, const u32x4_t* vd) __attribute__((always_inline)) {
+    auto consume = [&](int t, const u32x4_t (*kd)[CW], const u32x4_t (*vd)[CW]) __attribute__((always_inline)) {
         // scores of this lane's RPT rows for every head (log2 domain)
         float sc[G][RPT];
 #pragma unroll
@@ -184,16 +198,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) {
                 float part = 0.f;
-                if constexpr (BF) {
-                    const bf16x8_t k8 = __builtin_bit_cast(bf16x8_t, kd[k]);
-                    const bf16x8_t q8 = __builtin_bit_cast(bf16x8_t, qc[hh]);
-                    part = __builtin_amdgcn_fdot2_f32_bf16(pair<0>(k8), pair<0>(q8), part, false);
-                    part = __builtin_amdgcn_fdot2_f32_bf16(pair<1>(k8), pair<1>(q8), part, false);
-                    part = __builtin_amdgcn_fdot2_f32_bf16(pair<2>(k8), pair<2>(q8), part, false);
-                    part = __builtin_amdgcn_fdot2_f32_bf16(pair<3>(k8), pair<3>(q8), part, false);
-                } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) part = fmaf(__uint_as_float(kd[k][e]), __uint_as_float(qc[hh][e]), part);
+                for (int cw = 0; cw < CW; ++cw) {
+                    if constexpr (BF) {
+                        const bf16x8_t k8 = __builtin_bit_cast(bf16x8_t, kd[k][cw]);
+                        const bf16x8_t q8 = __builtin_bit_cast(bf16x8_t, qc[hh][cw]);
+                        part = __builtin_amdgcn_fdot2_f32_bf16(pair<0>(k8), pair<0>(q8), part, false);
+                        part = __builtin_amdgcn_fdot2_f32_bf16(pair<1>(k8), pair<1>(q8), part, false);
+                        part = __builtin_amdgcn_fdot2_f32_bf16(pair<2>(k8), pair<2>(q8), part, false);
+                        part = __builtin_amdgcn_fdot2_f32_bf16(pair<3>(k8), pair<3>(q8), part, false);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            part = fmaf(__uint_as_float(kd[k][cw][e]), __uint_as_float(qc[hh][cw][e]), part);
+                    }
                 }
                 const float dot = row_sum<CPR>(part);
                 sc[hh][k] = valid ? dot * c : -INFINITY;
@@ -220,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
             for (int hh = 0; hh < G; ++hh) {
                 l_h[hh] *= alpha[hh];
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) acc[hh][e] *= alpha[hh];
+                for (int e = 0; e < EPC * CW; ++e) acc[hh][e] *= alpha[hh];
             }
         }
         if constexpr (BF) {
@@ -228,12 +246,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
 #pragma unroll
             for (int k = 0; k < RPT; k += 2) {
                 // V values of rows k and k+1 interleaved per element
-                uint32_t lo[4], hi[4];
+                uint32_t lo[CW][4], hi[CW][4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    lo[e] = __builtin_amdgcn_perm(vd[k + 1][e], vd[k][e], 0x05040100u);
-                    hi[e] = __builtin_amdgcn_perm(vd[k + 1][e], vd[k][e], 0x07060302u);
-                }
+                for (int cw = 0; cw < CW; ++cw)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        lo[cw][e] = __builtin_amdgcn_perm(vd[k + 1][cw][e], vd[k][cw][e], 0x05040100u);
+                        hi[cw][e] = __builtin_amdgcn_perm(vd[k + 1][cw][e], vd[k][cw][e], 0x07060302u);
+                    }
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) {
                     const float mu = (m_h[hh] == -INFINITY) ? 0.f : m_h[hh];
@@ -241,12 +261,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
                                          (__bf16)__builtin_amdgcn_exp2f(sc[hh][k + 1] - mu)};
                     l_h[hh] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_h[hh], false);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        acc[hh][2 * e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lo[e]), pp,
-                                                                         acc[hh][2 * e], false);
-                        acc[hh][2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hi[e]), pp,
-                                                                             acc[hh][2 * e + 1], false);
-                    }
+                    for (int cw = 0; cw < CW; ++cw)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            float& a0 = acc[hh][cw * EPC + 2 * e];
+                            float& a1 = acc[hh][cw * EPC + 2 * e + 1];
+                            a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lo[cw][e]), pp, a0, false);
+                            a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hi[cw][e]), pp, a1, false);
+                        }
                 }
             }
         } else {
@@ -258,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
                     const float pr = __builtin_amdgcn_exp2f(sc[hh][k] - mu);
                     l_h[hh] += pr;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[hh][e] = fmaf(pr, __uint_as_float(vd[k][e]), acc[hh][e]);
+                    for (int e = 0; e < 4; ++e) acc[hh][e] = fmaf(pr, __uint_as_float(vd[k][0][e]), acc[hh][e]);
                 }
         }
     };
@@ -294,7 +316,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
         for (int r = 0; r < RG; ++r) M = fmaxf(M, sm_ml[r][hh][0]);
         wgt[hh] = (m_h[hh] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_h[hh] - M);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) sm_acc[rg][hh][dc * EPC + e] = acc[hh][e] * wgt[hh];
+        for (int cw = 0; cw < CW; ++cw)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) sm_acc[rg][hh][(dc + cw * CPR) * EPC + e] = acc[hh][cw * EPC + e] * wgt[hh];
     }
     __syncthreads();
     if (p.nsplit == 1) {
