@@ -585,9 +585,13 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
 //    K(t+3) and V(t+2), and waits only for the copies issued one step earlier;
 //  * this tile's probabilities, its P*V product and the next tile's scores
 //    form one straight-line block, 16 keys at a time, so that every matrix
-//    instruction has vector work of the same wave beside it.  The K fragments
-//    of each 16-key region are read from LDS one region ahead, and the
-//    region's V fragments before its score instructions;
+//    instruction has vector work of the same wave beside it.  The scores run
+//    one 16-key region ahead of P*V: the first region's score instructions
+//    are issued beside the short softmax head, and the last region masks the
+//    next score block and takes its row maximum beside this tile's last P*V
+//    instructions, so no stretch of the step is vector work alone.  The K
+//    fragments of a region are read from LDS two regions ahead, its V
+//    fragments just before its instructions;
 //  * the copies are buffer loads into LDS rather than global-segment loads:
 //    the latter are FLAT instructions that may also address LDS, and with
 //    one in flight the compiler's wait counting can no longer wait for a
@@ -905,13 +909,15 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             }
         }
     };
-    auto softmax_head = [&](f32x16_t* sc) __attribute__((always_inline)) {
+    auto tile_max = [&](const f32x16_t* sc) __attribute__((always_inline)) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
-        mx = partner_max(mx);
+        return partner_max(mx);
+    };
+    auto softmax_head = [&](float mx) __attribute__((always_inline)) {
         const float m_cand = fmaxf(m_run, mx * c);
         const bool grow = m_cand > m_run + 8.f;
         alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_cand) : 1.f;
@@ -939,19 +945,21 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             f.a[i] = *(const bf16x8_t*)(kl + k_lane + ((kb * 2 * CPR + 2 * cc) << 8));
         }
     };
+    // score instructions of one 16-key region (K fragments kf)
+    auto s_region = [&](int c2, const KFrag& kf, f32x16_t* sn) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NQF / 2; ++i) {
+            const int kb = i & 1, cc = c2 * (NQF / 4) + (i >> 1);
+            sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.a[i], qf[cc], sn[kb], 0, 0, 0);
+        }
+    };
     auto tile_work = [&](auto do_pv, auto do_s, f32x16_t* sc, f32x16_t* sn, const char* kl, const char* vl,
-                         KFrag& kf0) __attribute__((always_inline)) {
+                         KFrag& kf0, KFrag& kf1, auto finish_next) __attribute__((always_inline)) {
         constexpr bool DP = decltype(do_pv)::value, DS = decltype(do_s)::value;
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
         float rsv[4];
         bf16x8_t pb[4];
-        if constexpr (DS) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sn[kb][i] = 0.f;
-        }
         auto probs = [&](int c2) __attribute__((always_inline)) {
             u32x4_t pw;
             rsv[c2] = 0.f;
@@ -966,7 +974,8 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             pb[c2] = __builtin_bit_cast(bf16x8_t, pw);
             asm volatile("" : "+v"(rsv[c2]));  // keep the dot chain beside its exponentials
         };
-        KFrag kf1;
+        // region c2: P*V of region c2 and the scores of region c2 + 1 (the
+        // scores of region 0 were issued before the softmax head)
         auto mfmas = [&](int c2, const KFrag& kf) __attribute__((always_inline)) {
             u32x4_t vf[NDB];
             if constexpr (DP) {
@@ -979,13 +988,15 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
                 }
             }
             if constexpr (DS) {
-                if (c2 < 3) load_k(kl, c2 + 1, (c2 & 1) ? kf0 : kf1);
+                if (c2 < 2) load_k(kl, c2 + 2, (c2 & 1) ? kf1 : kf0);
             }
 #pragma unroll
             for (int i = 0; i < NQF / 2; ++i) {
                 if constexpr (DS) {
-                    const int kb = i & 1, cc = c2 * (NQF / 4) + (i >> 1);
-                    sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.a[i], qf[cc], sn[kb], 0, 0, 0);
+                    if (c2 < 3) {
+                        const int kb = i & 1, cc = (c2 + 1) * (NQF / 4) + (i >> 1);
+                        sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.a[i], qf[cc], sn[kb], 0, 0, 0);
+                    }
                 }
                 if constexpr (DP) {
                     const int db = i;
@@ -995,16 +1006,21 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             }
         };
         if constexpr (DP) probs(0);
+        float mx_next = 0.f;
 #pragma unroll
         for (int c2 = 0; c2 < 4; ++c2) {
             __builtin_amdgcn_sched_barrier(0);
-            mfmas(c2, (c2 & 1) ? kf1 : kf0);
+            // the last region masks the next block (edge tiles) and takes its
+            // row maximum beside this tile's last P*V instructions
+            if (c2 == 3) mx_next = finish_next();
+            mfmas(c2, (c2 & 1) ? kf0 : kf1);
             if constexpr (DP) {
                 if (c2 < 3) probs(c2 + 1);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (DP) l_run = l_run * alpha + ((rsv[0] + rsv[1]) + (rsv[2] + rsv[3]));
+        return mx_next;
     };
 
     const int n = ntiles;
@@ -1015,6 +1031,7 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     f32x16_t scur[2];
     scores(kb0, scur);
     mask_tile(0, scur);
+    float mx_cur = tile_max(scur);
     lds_barrier();  // tile 0's K reads are done before K(3) lands in kb0
     issue_k(min(1, n - 1), kb1);
     issue_v(0, vb0);
@@ -1027,13 +1044,25 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     auto step = [&](int t, const char* kn, const char* vc, char* ki, char* vi) __attribute__((always_inline)) {
         issue_k(min(t + 3, n - 1), ki);
         issue_v(min(t + 2, n - 1), vi);
-        KFrag kf0;
+        // K fragments of the next tile's first two regions; its first
+        // region's scores, then this tile's head (row maximum taken in the
+        // previous step)
+        KFrag kf0, kf1;
         load_k(kn, 0, kf0);
-        softmax_head(scur);
+        load_k(kn, 1, kf1);
         f32x16_t snext[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) snext[kb][i] = 0.f;
         // past the last tile the score block reads stale data and is discarded
-        tile_work(std::true_type{}, std::true_type{}, scur, snext, kn, vc, kf0);
-        if (t + 1 < n) mask_tile(t + 1, snext);
+        s_region(0, kf0, snext);
+        softmax_head(mx_cur);
+        mx_cur = tile_work(std::true_type{}, std::true_type{}, scur, snext, kn, vc, kf0, kf1,
+                           [&]() __attribute__((always_inline)) {
+                               if (t + 1 < n) mask_tile(t + 1, snext);
+                               return tile_max(snext);
+                           });
         scur[0] = snext[0];
         scur[1] = snext[1];
         wait_older_copies();
