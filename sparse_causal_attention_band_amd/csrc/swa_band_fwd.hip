@@ -42,6 +42,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
+#include <float.h>
 #include <type_traits>
 
 #include "swa_internal.h"
@@ -624,6 +625,7 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     constexpr int NQF = D / 16;                  // Q fragments
     static_assert(TILE_BYTES % 8192 == 0, "copy split");
     static_assert(NDB == NQF / 2, "one P*V instruction per score instruction");
+    static_assert(MODE == kBand || MODE == kChunk, "band tiles only: no compact (strided or listed) keys");
 
     __shared__ __attribute__((aligned(16))) char kb0[TILE_BYTES];
     __shared__ __attribute__((aligned(16))) char kb1[TILE_BYTES];
@@ -721,8 +723,9 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     // writes bytes 16i..16i+15 of a block).  Per block the lane's source is
     // a fixed byte offset inside the tile's 64 rows (K: row sigma(pos),
     // chunk ch; V: the swizzled quarter), so a tile whose rows are 64
-    // consecutive rows of one array costs one scalar base per tile.  Other
-    // tiles (the clamped diagonal tile, strided rows, a ring wrap or the
+    // consecutive rows of one array costs one scalar base per tile (in band
+    // mode every tile, the last key row bounding the resource).  In chunk
+    // mode other tiles (the diagonal tile at the end, a ring wrap or the
     // ring/chunk seam) take the general per-row path.
     uint32_t koff[NBLK], voff[NBLK];  // row * RB + byte in row; row = off / RB
 #pragma unroll
@@ -733,14 +736,6 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         koff[it] = (uint32_t)(sigma(pos) * RB + ((within >> 8) << 4));
         const int vr = P / RB;
         voff[it] = (uint32_t)(vr * RB + ((P % RB) ^ vswz(vr)));
-    }
-    // band mode: byte offset of the last key row plus the lane's byte in a row
-    // (the clamp of a copy's row to NK - 1, see issue_rows)
-    uint32_t klim[NBLK], vlim[NBLK];
-#pragma unroll
-    for (int it = 0; it < NBLK; ++it) {
-        klim[it] = (uint32_t)((NK - 1) * RB) + koff[it] % RB;
-        vlim[it] = (uint32_t)((NK - 1) * RB) + voff[it] % RB;
     }
     // The copies are buffer loads straight into LDS (MUBUF "lds" form).  A
     // resource covers one (sequence, KV head) array; the byte offset of a
@@ -773,22 +768,23 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             return 1;
         }
     };
-    auto issue_rows = [&](int t, char* dst, __amdgpu_buffer_rsrc_t rin, __amdgpu_buffer_rsrc_t rring,
-                          const uint32_t* off, const uint32_t* lim) __attribute__((always_inline)) {
+    auto issue_rows = [&](int t, char* dst, const elem_t* src, __amdgpu_buffer_rsrc_t rin,
+                          __amdgpu_buffer_rsrc_t rring, const uint32_t* off) __attribute__((always_inline)) {
         if constexpr (!CHUNK) {
             // Band mode: one copy instruction per block whatever the tile (a
             // branch between a contiguous and a gathered copy leaves the
             // compiler's copy tracking unsure at the join, and it then drains
-            // all copies before the next LDS read).  Row j0 + r clamped to
-            // NK - 1 is, in bytes, min(j0*RB + off, (NK-1)*RB + byte): the
-            // clamp is monotonic in the row and the byte within the row is
-            // the lane's own.
-            const uint32_t base = (uint32_t)((kt_hi - t) * kTileN * RB);
+            // all copies before the next LDS read).  The resource starts at
+            // the tile's first row and ends at the last key row, so the lane
+            // offsets are loop invariant and rows past the end read as zero
+            // (range-checked), which the mask and P = 0 make harmless.
+            const int j0 = (kt_hi - t) * kTileN;
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)j0 * D, (size_t)(NK - j0) * RB);
 #pragma unroll
             for (int it = 0; it < NBLK; ++it)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rin, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024), 16,
-                    (int)min(base + off[it], lim[it]), 0, 0, 0);
+                    r, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024), 16, (int)off[it], 0, 0,
+                    0);
             return;
         }
         int soff = 0;
@@ -827,8 +823,8 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             }
         }
     };
-    auto issue_k = [&](int t, char* kl) __attribute__((always_inline)) { issue_rows(t, kl, rk, rkr, koff, klim); };
-    auto issue_v = [&](int t, char* vl) __attribute__((always_inline)) { issue_rows(t, vl, rv, rvr, voff, vlim); };
+    auto issue_k = [&](int t, char* kl) __attribute__((always_inline)) { issue_rows(t, kl, kg, rk, rkr, koff); };
+    auto issue_v = [&](int t, char* vl) __attribute__((always_inline)) { issue_rows(t, vl, vg, rv, rvr, voff); };
     // Every step issues the same copies (past the end of the list the last
     // tile again, into a buffer nobody reads any more), so one fixed wait
     // count holds: the 2*NBLK loads of the current step may stay in flight.
@@ -839,7 +835,11 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    // m_run starts at the lowest finite value rather than -inf: a row with
+    // no allowed key yet then needs no special case (its scores are -inf,
+    // exp2(-inf + FLT_MAX) = 0), and the first finite tile maximum always
+    // grows it (alpha = exp2(-FLT_MAX - m) = 0)
+    float m_run = -FLT_MAX, l_run = 0.f;
     const float c = p.c;
     float alpha = 1.f;
 
@@ -956,23 +956,24 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     auto tile_work = [&](auto do_pv, auto do_s, f32x16_t* sc, f32x16_t* sn, const char* kl, const char* vl,
                          KFrag& kf0, KFrag& kf1, auto finish_next) __attribute__((always_inline)) {
         constexpr bool DP = decltype(do_pv)::value, DS = decltype(do_s)::value;
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        const float m_use = m_run;
         const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-        float rsv[4];
+        // one running row sum, started from the rescaled old one
+        float rs = 0.f;
+        if constexpr (DP) rs = l_run * alpha;
         bf16x8_t pb[4];
         auto probs = [&](int c2) __attribute__((always_inline)) {
             u32x4_t pw;
-            rsv[c2] = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float x0 = __builtin_amdgcn_exp2f(fmaf(sc[c2 >> 1][8 * (c2 & 1) + 2 * e], c, -m_use));
                 const float x1 = __builtin_amdgcn_exp2f(fmaf(sc[c2 >> 1][8 * (c2 & 1) + 2 * e + 1], c, -m_use));
                 const bf16x2_t pr = {(__bf16)x0, (__bf16)x1};
-                rsv[c2] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rsv[c2], false);
+                rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
                 pw[e] = __builtin_bit_cast(uint32_t, pr);
             }
             pb[c2] = __builtin_bit_cast(bf16x8_t, pw);
-            asm volatile("" : "+v"(rsv[c2]));  // keep the dot chain beside its exponentials
+            asm volatile("" : "+v"(rs));  // keep the dot chain beside its exponentials
         };
         // region c2: P*V of region c2 and the scores of region c2 + 1 (the
         // scores of region 0 were issued before the softmax head)
@@ -1019,11 +1020,20 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (DP) l_run = l_run * alpha + ((rsv[0] + rsv[1]) + (rsv[2] + rsv[3]));
+        if constexpr (DP) l_run = rs;
         return mx_next;
     };
 
     const int n = ntiles;
+    if constexpr (!CHUNK) {
+        // V(0) may end past the last key row; whether or not a range-checked
+        // copy writes its zeros, those rows of vb0 must hold finite values
+        // (they meet P = 0), so the buffer starts zeroed (the barrier below
+        // orders these writes before the copies)
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int it = 0; it < TILE_BYTES / (kThreads8 * 16); ++it) *(u32x4_t*)(vb0 + (it * kThreads8 + tid) * 16) = z;
+    }
     // prologue: K(0), scores of tile 0; then K(1), V(0), K(2), V(1) in flight
     issue_k(0, kb0);
     __builtin_amdgcn_s_waitcnt(0xF70);
