@@ -18,6 +18,10 @@ counts against the kernel).  The same line carries:
                   in-band TFLOP/s, and the ring append of the same chunk;
   * variants   -- the same layer under the two-sided band, differential
                   attention and global-token masks (in-band TFLOP/s);
+  * other_prefill -- the other two prefill workloads of the metric: the
+                  Gemma-3-shaped SWA-1024 forward at N=65536 (in-band TFLOP/s)
+                  and the local+strided mask at N=8192, which is small and
+                  HBM-bound (in-band TFLOP/s and GB/s of Q+K+V+O);
   * cpu_baseline -- the float64 oracle on the host cores over the whole
                   prefill workload (run before the GPU is touched, since its
                   worker pool forks).
@@ -186,6 +190,32 @@ def variant_legs(swa, inputs, torch, dev, args):
     return res
 
 
+def other_prefill_legs(swa, inputs, torch, dev, args):
+    """The Gemma-3-shaped SWA-1024 forward (B=2, 32/16 heads, N=65536) and
+    the local+strided forward (W=256 plus every 128th key, 16 heads, d=64,
+    N=8192), each timed like the main leg with fewer steps."""
+    res = {}
+    for cfg, steps in ((inputs.GEMMA, max(5, args.steps // 5)), (inputs.STRIDED, args.steps)):
+        q, k, v = (x.to(dev) for x in inputs.prefill_inputs(cfg))
+        out = torch.empty_like(q)
+        per, _ = time_launches(lambda i=0: swa.attn_fwd(q, k, v, window=cfg.window, stride=cfg.stride, out=out),
+                               steps, 10, torch)
+        ms = sum(per) / len(per)
+        fl = 4.0 * cfg.B * cfg.Hq * cfg.d * allowed_pairs(cfg.N, cfg.window, cfg.stride)
+        tf = fl / (ms * 1e-3) / 1e12
+        leg = {"value": round(tf, 2), "unit": "TFLOP/s", "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+               "avg_ms": round(ms, 4), "steps": steps, "algorithmic_flops": fl}
+        if cfg.stride:
+            # compulsory HBM bytes: Q and O per query head, K and V per KV head
+            nb = 2 * (2 * cfg.B * cfg.Hq + 2 * cfg.B * cfg.Hkv) * cfg.N * cfg.d
+            leg.update({"algorithmic_bytes": nb, "GB_s": round(nb / (ms * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        res[cfg.name] = leg
+        del q, k, v, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def time_launches(fn, steps, warmup, torch):
     for _ in range(warmup):
         fn()
@@ -215,6 +245,8 @@ def main():
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the two-sided, differential and global-token legs")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the Gemma-shaped and local+strided prefill legs")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -340,6 +372,8 @@ def main():
 
     if not args.no_variants:
         line["variants"] = variant_legs(swa, inputs, torch, dev, args)
+    if not args.no_other and args.workload == "mistral":
+        line["other_prefill"] = other_prefill_legs(swa, inputs, torch, dev, args)
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
