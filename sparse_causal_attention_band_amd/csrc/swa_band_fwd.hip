@@ -614,7 +614,6 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(PrefillParams p) {
-    constexpr bool STRIDED = MODE == kStrided;
     constexpr bool CHUNK = MODE == kChunk;
     using elem_t = uint16_t;
     constexpr int RB = D * 2;                    // bytes per K/V row
@@ -682,13 +681,7 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     asm volatile("" ::"s"(lam_ptr));
     const int kt_hi = min(NK - 1, qoff + q0 + BM - 1 + wr) / kTileN;
     const int kt_lo = max(0, qoff + q0 - W + 1) / kTileN;
-    const int nband = kt_hi - kt_lo + 1;
-    int M = 0, ncomp = 0;
-    if (STRIDED) {
-        M = (kt_lo * kTileN + p.stride - 1) / p.stride;
-        ncomp = (M + kTileN - 1) / kTileN;
-    }
-    const int ntiles = nband + ncomp;
+    const int ntiles = kt_hi - kt_lo + 1;
     const bool wave_live = qw0 < N;
 
     bf16x8_t qf[NQF];
@@ -716,9 +709,7 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     const int v_lane = v_row * RB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
     const int vq = vswz(v_row);
 
-    auto key_of = [&](int t, int r) __attribute__((always_inline)) {
-        return t < nband ? min((kt_hi - t) * kTileN + r, NK - 1) : min((t - nband) * kTileN + r, M - 1) * p.stride;
-    };
+    auto key_of = [&](int t, int r) __attribute__((always_inline)) { return min((kt_hi - t) * kTileN + r, NK - 1); };
     // copies: wave w fills 1 KiB blocks w, w+8, ... of the tile (lane i
     // writes bytes 16i..16i+15 of a block).  Per block the lane's source is
     // a fixed byte offset inside the tile's 64 rows (K: row sigma(pos),
@@ -750,7 +741,6 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     // tile t's rows as one run: 0 = gathered rows, 1 = input array at byte
     // offset soff, 2 = ring at soff
     auto tile_run = [&](int t, int& soff) __attribute__((always_inline)) {
-        if (t >= nband) return 0;
         const int j0 = (kt_hi - t) * kTileN;
         if (j0 + kTileN > NK) return 0;
         if constexpr (CHUNK) {
@@ -788,7 +778,7 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             return;
         }
         int soff = 0;
-        const int run = STRIDED ? 0 : tile_run(t, soff);
+        const int run = tile_run(t, soff);
         if (run != 0) {
             const __amdgpu_buffer_rsrc_t r = run == 1 ? rin : rring;
 #pragma unroll
@@ -856,34 +846,18 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         }
     };
     auto mask_tile = [&](int t, f32x16_t* sc) __attribute__((always_inline)) {
-        const bool band = t < nband;
         const int j0 = (kt_hi - t) * kTileN;
-        const bool edge = band ? !(j0 + kTileN - 1 <= qvw0 + wr && j0 >= qvw0 + kQw - W && j0 + kTileN <= NK)
-                               : ((t - nband + 1) * kTileN > M);
+        const bool edge = !(j0 + kTileN - 1 <= qvw0 + wr && j0 >= qvw0 + kQw - W && j0 + kTileN <= NK);
         if (edge) {
             // key of element i in block kb is j0 + 8g + C, C = kb*32 + 16*(i/8) + i%8;
             // with x = qv - j0 - 8g its distance is x - C, so each test is one
             // compare of a per-tile bound against a constant (the empty asm
             // keeps the compiler from turning them into 32 loop-invariant
             // per-lane constants)
-            int lo, hi, nk;
-            uint64_t sm = 0;
-            if (band) {
-                const int x = qv - j0 - 8 * g;
-                lo = x + wr;              // dist >= -wr  <=>  C <= lo
-                hi = x - W;               // dist < W     <=>  C > hi
-                nk = NK - j0 - 8 * g;     // key < NK     <=>  C < nk
-                if (STRIDED) {
-                    const int r0 = j0 % p.stride;
-                    uint64_t smask = 0;
-                    for (int o = r0 == 0 ? 0 : p.stride - r0; o < kTileN; o += p.stride) smask |= 1ull << o;
-                    sm = smask >> (8 * g);
-                }
-            } else {
-                lo = kTileN;
-                hi = kTileN;
-                nk = M - (t - nband) * kTileN - 8 * g;  // compact entry < M
-            }
+            const int x = qv - j0 - 8 * g;
+            int lo = x + wr;           // dist >= -wr  <=>  C <= lo
+            int hi = x - W;            // dist < W     <=>  C > hi
+            int nk = NK - j0 - 8 * g;  // key < NK     <=>  C < nk
             asm volatile("" : "+v"(lo), "+v"(hi), "+v"(nk));
             // which bounds this tile can violate (wave-uniform): most edge
             // tiles need one compare per element, not three
@@ -898,14 +872,12 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
                         sc[kb][i] = keep_of(C) ? sc[kb][i] : -INFINITY;
                     }
             };
-            if (!STRIDED && band && !need_hi && !need_nk) {
+            if (!need_hi && !need_nk) {
                 apply([&](int C) { return C <= lo; });
-            } else if (!STRIDED && band && !need_lo && !need_nk) {
+            } else if (!need_lo && !need_nk) {
                 apply([&](int C) { return C > hi; });
             } else {
-                apply([&](int C) {
-                    return band ? (C <= lo) & (C < nk) & ((C > hi) | (STRIDED & (((sm >> C) & 1ull) != 0))) : (C < nk);
-                });
+                apply([&](int C) { return (C <= lo) & (C < nk) & (C > hi); });
             }
         }
     };
