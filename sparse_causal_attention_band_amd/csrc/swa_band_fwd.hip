@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     auto issue_tile = [&](int t, char* kl, char* vl, bool do_k, bool do_v) __attribute__((always_inline)) {
         // key row behind tile row r (virtual index in chunk mode)
         auto key_of = [&](int r) __attribute__((always_inline)) {
-            if (t < nband) return min((kt_hi - t) * kTileN + r, NK - 1);
+            if (!KEYLIST || t < nband) return min((kt_hi - t) * kTileN + r, NK - 1);
             const int m = min((t - nband) * kTileN + r, M - 1);
             if constexpr (GLOBAL) return min(max(p.gidx[m], 0), NK - 1);
             return m * p.stride;
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
 
     // mask tile t: only tiles not entirely inside every row of this wave's band
     auto mask_tile = [&](int t, f32x16_t* sc) __attribute__((always_inline)) {
-        const bool band = t < nband;
+        const bool band = !KEYLIST || t < nband;  // (band and chunk modes have no compact tiles)
         const int j0 = (kt_hi - t) * kTileN;
         const bool edge = band ? !(j0 + kTileN - 1 <= qvw0 + wr && j0 >= qvw0 + kQw - W && j0 + kTileN <= NK)
                                : ((t - nband + 1) * kTileN > M);
