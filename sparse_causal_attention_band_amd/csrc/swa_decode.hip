@@ -163,18 +163,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     auto load = [&](int t, u32x4_t (*kd)[CW], u32x4_t (*vd)[CW]) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < RPT; ++k) {
-            const int slot = s0 + t * kTile + rg + RG * k;
-            const bool live = t < ntile && slot < s1;
+            // every lane loads (no branch: the compiler then counts the loads
+            // in flight exactly and keeps the next tiles' loads outstanding
+            // while this one is consumed); rows past the end read the last
+            // valid row again, whose score is masked and whose P is 0
+            const int slot = min(s0 + t * kTile + rg + RG * k, s1 - 1);
 #pragma unroll
             for (int c = 0; c < CW; ++c) {
-                u32x4_t kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-                if (live) {
-                    // read once per step: non-temporal loads stream past the caches
-                    kw = __builtin_nontemporal_load((const u32x4_t*)(kg + (size_t)slot * RB + c * CPR * 16));
-                    vw = __builtin_nontemporal_load((const u32x4_t*)(vg + (size_t)slot * RB + c * CPR * 16));
-                }
-                kd[k][c] = kw;
-                vd[k][c] = vw;
+                // read once per step: non-temporal loads stream past the caches
+                kd[k][c] = __builtin_nontemporal_load((const u32x4_t*)(kg + (size_t)slot * RB + c * CPR * 16));
+                vd[k][c] = __builtin_nontemporal_load((const u32x4_t*)(vg + (size_t)slot * RB + c * CPR * 16));
             }
         }
     };
@@ -288,13 +286,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams 
     // register ring: tiles t, t+1, ..., t+PD-1 are loaded before tile t is used
 #pragma unroll
     for (int j = 0; j < PD; ++j) load(j, kr[j], vr[j]);
+    // (no early exit inside a round: tiles past the end are all masked rows,
+    // and a loop body without branches lets the compiler keep the loads of
+    // the next tiles in flight across the round boundary)
     for (int t = 0; t < ntile; t += PD) {
 #pragma unroll
         for (int j = 0; j < PD; ++j) {
-            if (t + j < ntile) {
-                consume(t + j, kr[j], vr[j]);
-                load(t + j + PD, kr[j], vr[j]);
-            }
+            consume(t + j, kr[j], vr[j]);
+            load(t + j + PD, kr[j], vr[j]);
         }
     }
 
