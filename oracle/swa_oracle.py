@@ -236,6 +236,59 @@ def attn_fwd(q, k, v, window: int, stride: int = 0, scale: Optional[float] = Non
     return out
 
 
+
+def _head_lse_rows(q: np.ndarray, k: np.ndarray, rows: np.ndarray, window: int, stride: int,
+                   scale: float) -> np.ndarray:
+    """Row log-sum-exp of one (batch, head): ln sum_{j in S_i} exp(scale * q_i . k_j)
+    for each i in ``rows`` (float64), S_i the allowed set of ``_row_allowed``.
+
+    This is the natural log of the row's softmax denominator (SWA page §3.1,
+    the row-wise softmax over N_W(i)), taken with the row maximum factored
+    out so that no exponential overflows: m + ln sum exp(s - m)."""
+    out = np.empty(len(rows), dtype=np.float64)
+    if len(rows) == 0:
+        return out
+    block = 256
+    start = 0
+    while start < len(rows):
+        stop = start + 1
+        while stop < len(rows) and stop - start < block and rows[stop] == rows[stop - 1] + 1:
+            stop += 1
+        r = rows[start:stop]
+        keys = _block_keys(int(r[0]), int(r[-1]), window, stride)
+        scores = scale * (np.asarray(q[r], dtype=np.float64) @ np.asarray(k[keys], dtype=np.float64).T)
+        s = np.where(_row_allowed(r, keys, window, stride), scores, -np.inf)
+        m = s.max(axis=1)
+        out[start:stop] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+        start = stop
+    return out
+
+
+def attn_lse(q, k, window: int, stride: int = 0, scale: Optional[float] = None) -> np.ndarray:
+    """Row log-sum-exp of the band forward: float64 [B, Hq, N], entry (b, h, i)
+    = ln sum over the allowed keys j of row i of exp(scale * q[b,h,i] . k[b,h//G,j]).
+
+    Together with the output it lets two attention results over disjoint key
+    sets be merged exactly (weights exp(lse_1 - lse) and exp(lse_2 - lse), lse
+    the log of the summed denominators).  q: [B, Hq, N, d], k: [B, Hkv, N, d];
+    ``scale`` defaults to 1/sqrt(d)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    if q.ndim != 4 or k.ndim != 4 or k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]:
+        raise ValueError("q must be [B, Hq, N, d] and k [B, Hkv, N, d]")
+    if q.shape[1] % k.shape[1] != 0 or window < 1:
+        raise ValueError("Hq must be a multiple of Hkv and window >= 1")
+    B, Hq, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    G = Hq // k.shape[1]
+    rows = np.arange(N, dtype=np.int64)
+    out = np.empty((B, Hq, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            out[b, h] = _head_lse_rows(q[b, h], k[b, h // G], rows, window, stride, scale)
+    return out
+
 _POOL_INPUT = None
 
 
@@ -373,6 +426,30 @@ def chunk_prefill(q, k, v, kring, vring, p0, window: int, scale: Optional[float]
             vv = np.concatenate([vring[b, g][slots], v[b, g]])
             qq = np.concatenate([np.zeros((n_hist, d)), q[b, h]])
             out[b, h] = _head_rows(qq, kk, vv, n_hist + sel, window, 0, scale)
+    return out
+
+
+def chunk_prefill_lse(q, k, kring, p0, window: int, scale: Optional[float] = None) -> np.ndarray:
+    """Row log-sum-exp of chunked prefill (SWA page §4.3): float64 [B, Hq, T],
+    over the same keys as ``chunk_prefill`` (the ring history in time order,
+    then the chunk), i.e. the log of each chunk row's softmax denominator."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    kring = np.asarray(kring, dtype=np.float64)
+    B, Hq, T, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    G = Hq // k.shape[1]
+    out = np.empty((B, Hq, T), dtype=np.float64)
+    for b in range(B):
+        start = int(p0[b])
+        n_hist = min(start, window - 1)
+        slots = np.asarray([ring_slot(t, window) for t in range(start - n_hist + 1, start + 1)], dtype=np.int64)
+        for h in range(Hq):
+            g = h // G
+            kk = np.concatenate([kring[b, g][slots], k[b, g]])
+            qq = np.concatenate([np.zeros((n_hist, d)), q[b, h]])
+            out[b, h] = _head_lse_rows(qq, kk, n_hist + np.arange(T, dtype=np.int64), window, 0, scale)
     return out
 
 

@@ -357,6 +357,78 @@ def test_truncating_to_the_last_w_rows_is_not_the_rolling_cache():
     assert np.abs(two - two_cut).max() > 1e-3
 
 
+# ---------------------------------------------------------------- row log-sum-exp
+def test_lse_worked_example():
+    """SWA page §3.2: the exponentiated scores of position 5 are 1, 2, 3 under
+    W = 3 and 1, 1, 1, 2, 3 under full causal, so the row's softmax
+    denominators are 6 and 8; the zero queries of positions 1..4 give ln of
+    their key counts."""
+    g, k, v = _worked()
+    q = np.zeros(5)
+    q[4] = g["q5"]
+    lse = oracle.attn_lse(_as_bhnd(q), _as_bhnd(k), window=g["window_swa"], scale=1.0)[0, 0]
+    assert abs(lse[4] - math.log(6.0)) <= 1e-15
+    assert np.abs(lse[:4] - np.log([1.0, 2.0, 3.0, 3.0])).max() <= 1e-15
+    for w in (5, 6, 100):
+        full = oracle.attn_lse(_as_bhnd(q), _as_bhnd(k), window=w, scale=1.0)[0, 0]
+        assert abs(full[4] - math.log(8.0)) <= 1e-15
+        assert np.abs(full[:4] - np.log([1.0, 2.0, 3.0, 4.0])).max() <= 1e-15
+
+
+def test_lse_window_one_is_the_own_score():
+    rng = np.random.default_rng(5)
+    q, k = rng.standard_normal((2, 3, 17, 8)), rng.standard_normal((2, 3, 17, 8))
+    lse = oracle.attn_lse(q, k, window=1, scale=0.7)
+    assert np.abs(lse - 0.7 * (q * k).sum(-1)).max() <= 1e-12
+
+
+@pytest.mark.parametrize("n,w,s", [(30, 4, 0), (41, 6, 7), (20, 25, 3)])
+def test_lse_identical_keys_closed_form(n, w, s):
+    """Every key equal: the row's scores are all scale * q_i . k, so the
+    log-sum-exp is that score plus ln |S_i| (the allowed-set size)."""
+    rng = np.random.default_rng(n)
+    d = 4
+    q = rng.standard_normal((1, 2, n, d))
+    krow = rng.standard_normal(d)
+    k = np.broadcast_to(krow, (1, 1, n, d)).copy()
+    lse = oracle.attn_lse(q, k, window=w, stride=s, scale=0.5)
+    counts = np.array([len(oracle.allowed_set(i, w, s)) for i in range(n)], dtype=np.float64)
+    want = 0.5 * (q[0] @ krow) + np.log(counts)[None, :]
+    assert np.abs(lse[0] - want).max() <= 1e-12
+
+
+@pytest.mark.parametrize("n,w,s", [(24, 5, 0), (31, 4, 6)])
+def test_lse_reproduces_the_attention_weights(n, w, s):
+    """With V the identity (d_v = N) the forward's output row i is the
+    weight vector p_ij; it must equal exp(scale * s_ij - lse_i) on the
+    allowed keys and 0 elsewhere (d = N so that V may be the identity)."""
+    rng = np.random.default_rng(n + w)
+    d = n
+    q, k = 0.3 * rng.standard_normal((1, 1, n, d)), rng.standard_normal((1, 1, n, d))
+    v = np.eye(n).reshape(1, 1, n, n)
+    p = oracle.attn_fwd(q, k, v, w, s, 0.8)[0, 0]
+    lse = oracle.attn_lse(q, k, w, s, 0.8)[0, 0]
+    allowed = oracle.allowed_mask(n, w, s)
+    want = np.where(allowed, np.exp(0.8 * (q[0, 0] @ k[0, 0].T) - lse[:, None]), 0.0)
+    assert np.abs(p - want).max() <= 1e-12
+
+
+@pytest.mark.parametrize("W,p0,T", [(8, 0, 5), (8, 3, 6), (8, 20, 9), (16, 7, 40)])
+def test_chunk_lse_equals_whole_sequence_lse(W, p0, T):
+    """Chunked prefill over a ring holding positions 1..p0 has, row for row,
+    the log-sum-exp of the whole sequence's last T rows (SWA page §4.3)."""
+    rng = np.random.default_rng(W * 100 + p0)
+    d, n = 4, p0 + T
+    q = rng.standard_normal((1, 2, n, d))
+    k = rng.standard_normal((1, 1, n, d))
+    kring = np.zeros((1, 1, W, d))
+    for t in range(1, p0 + 1):
+        kring[0, 0, oracle.ring_slot(t, W)] = k[0, 0, t - 1]
+    got = oracle.chunk_prefill_lse(q[:, :, p0:], k[:, :, p0:], kring, [p0], W, scale=0.9)
+    want = oracle.attn_lse(q, k, W, 0, 0.9)[:, :, p0:]
+    assert np.abs(got - want).max() <= 1e-12
+
+
 # ---------------------------------------------------------------- pin strength
 def _pins_fail(monkeypatch, name, bad):
     """Run the pins with one oracle helper replaced; True if any pin fails."""
@@ -365,7 +437,8 @@ def _pins_fail(monkeypatch, name, bad):
               test_window_one_returns_v, test_rows_sum_to_one_and_zero_outside_mask,
               test_full_causal_equals_library_and_is_bitwise_stable_in_W,
               lambda: test_band_and_strided_equal_library_with_explicit_mask(70, 9, 8),
-              test_zero_query_is_mean_of_allowed_values]
+              test_zero_query_is_mean_of_allowed_values, test_lse_worked_example,
+              lambda: test_lse_identical_keys_closed_form(41, 6, 7)]
     failed = False
     for c in checks:
         try:
