@@ -79,6 +79,25 @@ SWA_API int swa_attn_fwd_f32(const float* q, const float* k, const float* v, flo
                      int window, int stride, float scale, hipStream_t stream);
 
 /*
+ * swa_attn_fwd plus the row log-sum-exp: lse[b][h][i] = ln of row i's softmax
+ * denominator, ln sum over the allowed keys j of exp(scale * q_i . k_j) (the
+ * row-wise softmax of the SWA page, §3.1), in fp32.  With it, results over
+ * disjoint key sets merge exactly: o = (e1 o1 + e2 o2) / (e1 + e2) with
+ * e_x = exp(lse_x - max(lse_1, lse_2)).
+ *   lse : float [B, Hq, N] on the device, non-null, 4-byte aligned, not
+ *         overlapping q, k, v or out.  Everything else as swa_attn_fwd; out
+ *         is the same (bitwise) as swa_attn_fwd writes.
+ */
+SWA_API int swa_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int B, int Hq, int Hkv, int N, int d,
+                     int window, int stride, float scale, hipStream_t stream);
+
+/* Same contract with fp32 tensors and fp32 matrix-core arithmetic. */
+SWA_API int swa_attn_fwd_lse_f32(const float* q, const float* k, const float* v, float* out, float* lse,
+                     int B, int Hq, int Hkv, int N, int d,
+                     int window, int stride, float scale, hipStream_t stream);
+
+/*
  * One decode step per sequence over a rolling window-slot KV cache.
  * Absolute position t (1-based) lives in ring slot (t-1) % window, the rule
  * of the SWA page (§4.2); slot order is not time order, and since the
@@ -212,6 +231,21 @@ SWA_API int swa_chunk_prefill(const void* q, const void* k, const void* v, const
 SWA_API int swa_chunk_prefill_f32(const float* q, const float* k, const float* v, const float* kring,
                                   const float* vring, const int32_t* p0, float* out, int B, int Hq, int Hkv, int T,
                                   int d, int window, float scale, hipStream_t stream);
+
+/*
+ * swa_chunk_prefill plus the row log-sum-exp of each chunk row over the keys
+ * it reads (history and chunk), as for swa_attn_fwd_lse.
+ *   lse : float [B, Hq, T] on the device, non-null, 4-byte aligned, not
+ *         overlapping out.  Everything else as swa_chunk_prefill.
+ */
+SWA_API int swa_chunk_prefill_lse(const void* q, const void* k, const void* v, const void* kring, const void* vring,
+                                  const int32_t* p0, void* out, float* lse, int B, int Hq, int Hkv, int T, int d,
+                                  int window, float scale, hipStream_t stream);
+
+/* Same contract with fp32 tensors and fp32 matrix-core arithmetic. */
+SWA_API int swa_chunk_prefill_lse_f32(const float* q, const float* k, const float* v, const float* kring,
+                                      const float* vring, const int32_t* p0, float* out, float* lse, int B, int Hq,
+                                      int Hkv, int T, int d, int window, float scale, hipStream_t stream);
 
 /*
  * Rolling-cache append (SWA page §4.2): chunk row r of sequence b (absolute

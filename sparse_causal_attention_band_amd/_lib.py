@@ -30,6 +30,8 @@ _Z = ctypes.c_size_t
 SIGNATURES = {
     "swa_attn_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_attn_fwd_f32": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "swa_attn_fwd_lse": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "swa_attn_fwd_lse_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _Z, _I, _P]),
     "swa_decode_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _Z, _I, _P]),
     "swa_attn_fwd_two_sided": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
@@ -41,6 +43,8 @@ SIGNATURES = {
     "swa_attn_fwd_global_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
     "swa_chunk_prefill": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_chunk_prefill_f32": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "swa_chunk_prefill_lse": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "swa_chunk_prefill_lse_f32": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_ring_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "swa_ring_append_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "swa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
@@ -97,11 +101,13 @@ def _need(t: torch.Tensor, name: str, dtype, device):
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: int, stride: int = 0,
-             scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+             scale: float | None = None, out: torch.Tensor | None = None, return_lse: bool = False):
     """Causal sliding-window (optionally + strided) attention forward.
 
     q: [B, Hq, N, d], k/v: [B, Hkv, N, d], all bf16 (or all fp32) on one GPU.
     Returns out [B, Hq, N, d] in the input dtype.  scale defaults to 1/sqrt(d).
+    With ``return_lse`` returns (out, lse), lse fp32 [B, Hq, N] the natural
+    log of each row's softmax denominator.
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H, N, d]")
@@ -122,6 +128,12 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: int, str
         raise ValueError("out must have q's shape")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if return_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+        fn = lib().swa_attn_fwd_lse if dtype == torch.bfloat16 else lib().swa_attn_fwd_lse_f32
+        _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, k.shape[1], N, d,
+                  int(window), int(stride), float(scale), _stream(dev)))
+        return out, lse
     fn = lib().swa_attn_fwd if dtype == torch.bfloat16 else lib().swa_attn_fwd_f32
     _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, k.shape[1], N, d,
               int(window), int(stride), float(scale), _stream(dev)))
@@ -285,12 +297,14 @@ def decode(q: torch.Tensor, kring: torch.Tensor, vring: torch.Tensor, pos: torch
 
 
 def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kring: torch.Tensor, vring: torch.Tensor,
-                  p0: torch.Tensor, scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+                  p0: torch.Tensor, scale: float | None = None, out: torch.Tensor | None = None,
+                  return_lse: bool = False):
     """A chunk of new tokens over the rolling-cache history plus itself.
 
     q: [B, Hq, T, d]; k, v: [B, Hkv, T, d]; kring, vring: [B, Hkv, W, d]
     holding positions up to p0 (int32 [B] on the GPU).  Call before
-    ``ring_append`` of the same chunk.
+    ``ring_append`` of the same chunk.  With ``return_lse`` returns (out, lse),
+    lse fp32 [B, Hq, T] as for ``attn_fwd``.
     """
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or kring.dim() != 4 or vring.shape != kring.shape:
         raise ValueError("q, k, v must be [B, H, T, d] and kring, vring [B, Hkv, W, d]")
@@ -316,6 +330,13 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kring: torc
         raise ValueError("out must have q's shape")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if return_lse:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+        fn = lib().swa_chunk_prefill_lse if dtype == torch.bfloat16 else lib().swa_chunk_prefill_lse_f32
+        _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), kring.data_ptr(), vring.data_ptr(), p0.data_ptr(),
+                  out.data_ptr(), lse.data_ptr(), B, Hq, k.shape[1], T, d, kring.shape[2], float(scale),
+                  _stream(dev)))
+        return out, lse
     fn = lib().swa_chunk_prefill if dtype == torch.bfloat16 else lib().swa_chunk_prefill_f32
     _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), kring.data_ptr(), vring.data_ptr(), p0.data_ptr(),
               out.data_ptr(), B, Hq, k.shape[1], T, d, kring.shape[2], float(scale), _stream(dev)))

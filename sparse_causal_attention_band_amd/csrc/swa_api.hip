@@ -45,7 +45,7 @@ int check_scale(const char* name, float scale) {
 // min(N-1, i+right), plus the multiples of stride below the band.
 int band_fwd(bool bf16, const char* name, const void* q, const void* k, const void* v, void* out, int B, int Hq,
              int Hkv, int N, int d, int window, int right, int stride, float scale, hipStream_t stream,
-             const float* lam = nullptr, const int32_t* gidx = nullptr, int ng = 0) {
+             const float* lam = nullptr, const int32_t* gidx = nullptr, int ng = 0, float* lse = nullptr) {
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1)
         return fail(SWA_ERR_INVALID_ARG, "%s: B, N, Hq, Hkv must be >= 1 (B=%d N=%d Hq=%d Hkv=%d)", name, B, N, Hq,
                     Hkv);
@@ -65,6 +65,13 @@ int band_fwd(bool bf16, const char* name, const void* q, const void* k, const vo
     };
     if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k, kbytes) || overlap(out, qbytes, v, kbytes))
         return fail(SWA_ERR_INVALID_ARG, "%s: out must not overlap q, k or v", name);
+    if (lse != nullptr) {
+        const long long lbytes = (long long)B * Hq * N * 4;
+        if ((uintptr_t)lse & 3u) return fail(SWA_ERR_INVALID_ARG, "%s: lse must be 4-byte aligned", name);
+        if (overlap(lse, lbytes, out, qbytes) || overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kbytes) ||
+            overlap(lse, lbytes, v, kbytes))
+            return fail(SWA_ERR_INVALID_ARG, "%s: lse must not overlap q, k, v or out", name);
+    }
     const long long G = Hq / Hkv;
     const long long rows = (long long)N * d;
     if ((long long)B * Hq * rows > (1ll << 40)) return fail(SWA_ERR_UNSUPPORTED, "%s: tensor too large", name);
@@ -78,6 +85,7 @@ int band_fwd(bool bf16, const char* name, const void* q, const void* k, const vo
     p.vring = nullptr;
     p.p0 = nullptr;
     p.lam = lam;
+    p.lse = lse;
     p.gidx = gidx;
     p.ng = ng;
     p.B = B;
@@ -104,6 +112,14 @@ int attn_fwd(bool bf16, const void* q, const void* k, const void* v, void* out, 
              int d, int window, int stride, float scale, hipStream_t stream) {
     return band_fwd(bf16, bf16 ? "swa_attn_fwd" : "swa_attn_fwd_f32", q, k, v, out, B, Hq, Hkv, N, d, window, 0,
                     stride, scale, stream);
+}
+
+int attn_fwd_lse(bool bf16, const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+                 int Hkv, int N, int d, int window, int stride, float scale, hipStream_t stream) {
+    const char* name = bf16 ? "swa_attn_fwd_lse" : "swa_attn_fwd_lse_f32";
+    if (lse == nullptr) return fail(SWA_ERR_INVALID_ARG, "%s: lse must be non-null", name);
+    return band_fwd(bf16, name, q, k, v, out, B, Hq, Hkv, N, d, window, 0, stride, scale, stream, nullptr, nullptr, 0,
+                    lse);
 }
 
 int two_sided_fwd(bool bf16, const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int N,
@@ -203,8 +219,8 @@ int global_fwd(bool bf16, const void* q, const void* k, const void* v, void* out
 
 int chunk_prefill(bool bf16, const void* q, const void* k, const void* v, const void* kring, const void* vring,
                   const int32_t* p0, void* out, int B, int Hq, int Hkv, int T, int d, int window, float scale,
-                  hipStream_t stream) {
-    const char* name = bf16 ? "swa_chunk_prefill" : "swa_chunk_prefill_f32";
+                  hipStream_t stream, float* lse = nullptr, const char* name = nullptr) {
+    if (name == nullptr) name = bf16 ? "swa_chunk_prefill" : "swa_chunk_prefill_f32";
     if (B < 1 || T < 1 || Hq < 1 || Hkv < 1)
         return fail(SWA_ERR_INVALID_ARG, "%s: B, T, Hq, Hkv must be >= 1 (B=%d T=%d Hq=%d Hkv=%d)", name, B, T, Hq,
                     Hkv);
@@ -217,6 +233,14 @@ int chunk_prefill(bool bf16, const void* q, const void* k, const void* v, const 
         return fail(SWA_ERR_INVALID_ARG, "%s: p0 must be non-null, 4-byte aligned", name);
     if (int rc = check_scale(name, scale)) return rc;
     if ((long long)T + window > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: T + window too large", name);
+    if (lse != nullptr && ((uintptr_t)lse & 3u)) return fail(SWA_ERR_INVALID_ARG, "%s: lse must be 4-byte aligned", name);
+    if (lse != nullptr) {
+        const char* l0 = (const char*)lse;
+        const long long lbytes = (long long)B * Hq * T * 4, obytes = (long long)B * Hq * T * d * (bf16 ? 2 : 4);
+        const char* o0 = (const char*)out;
+        if (l0 < o0 + obytes && o0 < l0 + lbytes)
+            return fail(SWA_ERR_INVALID_ARG, "%s: lse must not overlap out", name);
+    }
     const long long G = Hq / Hkv;
     swa::PrefillParams p{};
     p.q = q;
@@ -227,6 +251,7 @@ int chunk_prefill(bool bf16, const void* q, const void* k, const void* v, const 
     p.vring = vring;
     p.p0 = p0;
     p.lam = nullptr;
+    p.lse = lse;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
@@ -323,6 +348,16 @@ int swa_attn_fwd_f32(const float* q, const float* k, const float* v, float* out,
     return attn_fwd(false, q, k, v, out, B, Hq, Hkv, N, d, window, stride, scale, stream);
 }
 
+int swa_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int N,
+                     int d, int window, int stride, float scale, hipStream_t stream) {
+    return attn_fwd_lse(true, q, k, v, out, lse, B, Hq, Hkv, N, d, window, stride, scale, stream);
+}
+
+int swa_attn_fwd_lse_f32(const float* q, const float* k, const float* v, float* out, float* lse, int B, int Hq,
+                         int Hkv, int N, int d, int window, int stride, float scale, hipStream_t stream) {
+    return attn_fwd_lse(false, q, k, v, out, lse, B, Hq, Hkv, N, d, window, stride, scale, stream);
+}
+
 int swa_decode(const void* q, const void* kring, const void* vring, const int32_t* pos, void* out, int B, int Hq,
                int Hkv, int d, float scale, void* workspace, size_t workspace_bytes, int window, hipStream_t stream) {
     return decode(true, q, kring, vring, pos, out, B, Hq, Hkv, d, scale, workspace, workspace_bytes, window, stream);
@@ -383,6 +418,22 @@ int swa_chunk_prefill_f32(const float* q, const float* k, const float* v, const 
                           const int32_t* p0, float* out, int B, int Hq, int Hkv, int T, int d, int window,
                           float scale, hipStream_t stream) {
     return chunk_prefill(false, q, k, v, kring, vring, p0, out, B, Hq, Hkv, T, d, window, scale, stream);
+}
+
+int swa_chunk_prefill_lse(const void* q, const void* k, const void* v, const void* kring, const void* vring,
+                          const int32_t* p0, void* out, float* lse, int B, int Hq, int Hkv, int T, int d, int window,
+                          float scale, hipStream_t stream) {
+    if (lse == nullptr) return fail(SWA_ERR_INVALID_ARG, "swa_chunk_prefill_lse: lse must be non-null");
+    return chunk_prefill(true, q, k, v, kring, vring, p0, out, B, Hq, Hkv, T, d, window, scale, stream, lse,
+                         "swa_chunk_prefill_lse");
+}
+
+int swa_chunk_prefill_lse_f32(const float* q, const float* k, const float* v, const float* kring, const float* vring,
+                              const int32_t* p0, float* out, float* lse, int B, int Hq, int Hkv, int T, int d,
+                              int window, float scale, hipStream_t stream) {
+    if (lse == nullptr) return fail(SWA_ERR_INVALID_ARG, "swa_chunk_prefill_lse_f32: lse must be non-null");
+    return chunk_prefill(false, q, k, v, kring, vring, p0, out, B, Hq, Hkv, T, d, window, scale, stream, lse,
+                         "swa_chunk_prefill_lse_f32");
 }
 
 int swa_ring_append(const void* k, const void* v, const int32_t* p0, void* kring, void* vring, int B, int Hkv, int T,

@@ -535,6 +535,12 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
     // ---- epilogue: O / l, lane holds d = 32*db + 8*quad + 4*g + 0..3
     const float lt = partner_sum(l_run);
     if (!wave_live || qi >= N) return;
+    if (p.lse != nullptr && g == 0) {
+        // ln of the row's softmax denominator: the exponentials were taken
+        // relative to m_use in log2 units of scale * q.k
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        p.lse[(size_t)(b * p.Hq + h) * N + qi] = (m_use + __log2f(lt)) * 0.69314718055994531f;
+    }
     // plain store, or (second map of differential attention) out -= lam * O/l
     const bool sub = p.lam != nullptr;
     const float inv = (sub ? -p.lam[h] : 1.f) / lt;
@@ -678,7 +684,8 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     // tile loop: a scalar load still in flight there would force every LDS
     // wait in the loop to drain all outstanding reads
     const float* lam_ptr = p.lam;
-    asm volatile("" ::"s"(lam_ptr));
+    float* lse_ptr = p.lse;
+    asm volatile("" ::"s"(lam_ptr), "s"(lse_ptr));
     const int kt_hi = min(NK - 1, qoff + q0 + BM - 1 + wr) / kTileN;
     const int kt_lo = max(0, qoff + q0 - W + 1) / kTileN;
     const int ntiles = kt_hi - kt_lo + 1;
@@ -1063,8 +1070,10 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
 
     const float lt = partner_sum(l_run);
     if (!wave_live || qi >= N) return;
-    const bool sub = p.lam != nullptr;  // differential attention: out -= lam * O/l
-    const float inv = (sub ? -p.lam[h] : 1.f) / lt;
+    if (lse_ptr != nullptr && g == 0)  // ln of the row's softmax denominator (see the 4-wave kernel)
+        lse_ptr[(size_t)(b * p.Hq + h) * N + qi] = (m_run + __log2f(lt)) * 0.69314718055994531f;
+    const bool sub = lam_ptr != nullptr;  // differential attention: out -= lam * O/l
+    const float inv = (sub ? -lam_ptr[h] : 1.f) / lt;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll

@@ -20,6 +20,7 @@ struct PrefillParams {
     const void* vring;
     const int32_t* p0;     // chunk mode: [B] positions already cached
     const float* lam;      // non-null: out -= lam[h] * result (second map of differential attention)
+    float* lse;            // non-null: [B, Hq, N] row log-sum-exp (natural log of the softmax denominator)
     const int32_t* gidx;   // global mode: sorted global positions [ng]
     int ng;
     int B, Hq, Hkv, N;

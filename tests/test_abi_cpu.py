@@ -152,3 +152,22 @@ def test_global_rejects_bad_arguments_and_sizes_its_workspace():
     # -> 64 splits of 64-key tiles over N = 4096 keys, d + 2 floats each
     assert L.swa_attn_fwd_global_workspace_bytes(1, 8, 2, 4096, 128, 4) == 4 * 8 * 64 * 130 * 4
     assert L.swa_attn_fwd_global_workspace_bytes(1, 8, 2, 4096, 128, 0) == 0
+
+
+def test_lse_entry_points_reject_bad_arguments():
+    L = swa.lib()
+    base = (A, A * 2, A * 3, A * 1024)
+    sizes = (1, 4, 2, 16, 64, 4, 0, 0.125, None)
+    assert L.swa_attn_fwd_lse(*base, None, *sizes) == -1              # lse missing
+    assert L.swa_attn_fwd_lse(*base, A * 2048 + 2, *sizes) == -1      # misaligned
+    assert L.swa_attn_fwd_lse(*base, A * 1024 + 64, *sizes) == -1     # inside out
+    assert L.swa_last_error().decode().startswith("swa_attn_fwd_lse")
+    assert L.swa_attn_fwd_lse_f32(*base, None, *sizes) == -1
+    assert L.swa_last_error().decode().startswith("swa_attn_fwd_lse_f32")
+    ch = (A, A * 2, A * 3, A * 4, A * 5, A * 6, A * 1024)
+    csz = (1, 4, 2, 16, 64, 8, 0.125, None)
+    assert L.swa_chunk_prefill_lse(*ch, None, *csz) == -1
+    assert L.swa_chunk_prefill_lse(*ch, A * 2048 + 1, *csz) == -1
+    assert L.swa_chunk_prefill_lse(*ch, A * 1024 + 4, *csz) == -1
+    assert L.swa_last_error().decode().startswith("swa_chunk_prefill_lse")
+    assert L.swa_chunk_prefill_lse_f32(*ch, None, *csz) == -1
