@@ -34,6 +34,10 @@
  *  - Outputs are deterministic: fixed reduction order, no float atomics.
  *  - Calls on different streams may run concurrently; a workspace must not be
  *    shared by calls that may overlap.
+ *  - The header is plain C (C99 and later, or C++).  It includes the HIP
+ *    runtime API header for hipStream_t, so a program compiled by a host
+ *    compiler rather than hipcc defines __HIP_PLATFORM_AMD__, as for any HIP
+ *    API use, and links libswa_attn.so.
  */
 #ifndef SWA_ATTN_H
 #define SWA_ATTN_H

@@ -1,0 +1,63 @@
+"""The public header is a C ABI: a plain C99 program (gcc, no C++ and no
+hipcc) includes include/swa_attn.h, links the built library and gets the
+documented error codes from host-side validation.  No GPU is touched: every
+call below is rejected before anything is enqueued."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIBDIR = os.path.join(ROOT, "sparse_causal_attention_band_amd")
+
+SRC = r"""
+#include "swa_attn.h"
+#include <stdio.h>
+#include <string.h>
+
+static int expect(int rc, int want, const char* prefix) {
+    const char* msg = swa_last_error();
+    if (rc != want || strncmp(msg, prefix, strlen(prefix)) != 0) {
+        printf("FAIL rc=%d want=%d msg=%s\n", rc, want, msg);
+        return 1;
+    }
+    return 0;
+}
+
+int main(void) {
+    char* a = (char*)(uintptr_t)4096;  /* aligned fake device addresses, never dereferenced */
+    int bad = 0;
+    bad |= expect(swa_attn_fwd(NULL, a, a, a, 1, 4, 2, 16, 64, 4, 0, 0.125f, NULL), SWA_ERR_INVALID_ARG, "swa_attn_fwd");
+    bad |= expect(swa_attn_fwd(a, a + 8192, a + 16384, a + 65536, 1, 4, 2, 16, 96, 4, 0, 0.125f, NULL),
+                  SWA_ERR_UNSUPPORTED, "swa_attn_fwd");
+    bad |= expect(swa_attn_fwd_lse(a, a + 8192, a + 16384, a + 65536, NULL, 1, 4, 2, 16, 64, 4, 0, 0.125f, NULL),
+                  SWA_ERR_INVALID_ARG, "swa_attn_fwd_lse");
+    bad |= expect(swa_decode(a, a, a, NULL, a, 2, 8, 2, 128, 0.1f, NULL, 0, 4096, NULL), SWA_ERR_INVALID_ARG,
+                  "swa_decode");
+    /* 512 (sequence, KV head) pairs: one split, no workspace; 4 pairs: split */
+    if (swa_decode_workspace_bytes(64, 32, 8, 128, 4096) != 0) bad = 1;
+    if (swa_decode_workspace_bytes(2, 8, 2, 128, 4096) == 0) bad = 1;
+    printf(bad ? "FAILED\n" : "OK\n");
+    return bad;
+}
+"""
+
+
+def test_plain_c_program_uses_the_abi(tmp_path):
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    if not os.path.exists(os.path.join(LIBDIR, "libswa_attn.so")):
+        pytest.skip("library not built")
+    src = tmp_path / "consumer.c"
+    src.write_text(SRC)
+    exe = tmp_path / "consumer"
+    # any HIP API consumer built without hipcc names its platform
+    cmd = [gcc, "-std=c99", "-Wall", "-Werror", "-Wno-error=pedantic", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", str(src), "-o", str(exe),
+           "-L", LIBDIR, "-lswa_attn", "-Wl,-rpath," + LIBDIR]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip().endswith("OK"), r.stdout + r.stderr
