@@ -117,8 +117,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
 
 // MODE: kBand (window only), kStrided (window + multiples of the stride),
 // kChunk (a chunk of new queries over the ring history plus the chunk).
+// The bf16 d = 64 strided instantiation is held to three waves per SIMD (168
+// registers; its extra mask paths would otherwise take 170, i.e. two waves):
+// short windows make most of its tiles edge tiles, and three workgroups per
+// CU hide more of each tile's latency.  The other modes run faster without
+// the cap (band and chunk at two waves; global spills under it).
 template <bool BF, int D, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, (BF && D == 64 && MODE == kStrided) ? 3 : 2) void
+band_fwd_kernel(PrefillParams p) {
     constexpr bool STRIDED = MODE == kStrided;
     constexpr bool CHUNK = MODE == kChunk;
     constexpr bool GLOBAL = MODE == kGlobal;
@@ -391,10 +397,17 @@ __global__ __launch_bounds__(kThreads, 2) void band_fwd_kernel(PrefillParams p) 
                         sc[kb][i] = keep_of(C) ? sc[kb][i] : -INFINITY;
                     }
             };
-            if (!KEYLIST && band && !need_hi && !need_nk) {
+            if (band && !need_hi && !need_nk) {
+                // every key of the tile lies inside every row's window, so an
+                // extra (strided or global) key changes nothing: causal bound only
                 apply([&](int C) { return C <= lo; });
-            } else if (!KEYLIST && band && !need_lo && !need_nk) {
-                apply([&](int C) { return C > hi; });
+            } else if (band && !need_lo && !need_nk) {
+                // every key is causal for every row: the window's lower
+                // bound, or an extra key below it
+                if constexpr (KEYLIST)
+                    apply([&](int C) { return (C > hi) | (((sm >> C) & 1ull) != 0); });
+                else
+                    apply([&](int C) { return C > hi; });
             } else {
                 // non-short-circuit operators: a straight-line select, no
                 // per-element divergent branches.  (Keys past the end exist
