@@ -665,22 +665,31 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     const int kvh = rest % p.Hkv;
     const int b = rest / p.Hkv;
     const int N = p.N;
-    int qoff = 0, hslot0 = 0;
+    // Chunk mode: the virtual key sequence is [placeholders | history |
+    // chunk].  The qoff = min(start, W-1) history keys come from the ring
+    // (older positions are outside every row's window); kmin < 64
+    // placeholder keys before them put the chunk's first row at the start of
+    // a 64-key tile, so that no tile mixes ring and chunk rows and every
+    // tile's copy has a single source.  Placeholders are masked like keys
+    // below the window.  Band mode: the sequence is the input (qbase = 0).
+    int qoff = 0, hslot0 = 0, kmin = 0;
     if constexpr (CHUNK) {
         // uniform per workgroup: scalar registers, so the copy offsets stay scalar
         const int start = __builtin_amdgcn_readfirstlane(max(p.p0[b], 0));
         qoff = min(start, p.W - 1);
-        hslot0 = (start - qoff) % p.W;
+        hslot0 = (start - qoff) % p.W;  // ring slot of history entry 0
+        kmin = (-qoff) & (kTileN - 1);
     }
-    const int NK = qoff + N;
+    const int qbase = kmin + qoff;  // virtual position of query row 0
+    const int NK = qbase + N;
     const int W = min(p.W, NK);
     const int BM = kQw * p.PB;
     const int q0 = qb * BM;
     const int h = kvh * p.G + hg * p.HG + (wave % p.HG);
     const int qw0 = q0 + kQw * (wave / p.HG);
     const int qi = qw0 + l32;
-    const int qv = qoff + qi;
-    const int qvw0 = qoff + qw0;
+    const int qv = qbase + qi;
+    const int qvw0 = qbase + qw0;
 
     const size_t kv_head = (size_t)(b * p.Hkv + kvh) * (size_t)N * D;
     const size_t q_head = (size_t)(b * p.Hq + h) * (size_t)N * D;
@@ -699,8 +708,8 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     const float* lam_ptr = p.lam;
     float* lse_ptr = p.lse;
     asm volatile("" ::"s"(lam_ptr), "s"(lse_ptr));
-    const int kt_hi = min(NK - 1, qoff + q0 + BM - 1 + wr) / kTileN;
-    const int kt_lo = max(0, qoff + q0 - W + 1) / kTileN;
+    const int kt_hi = min(NK - 1, qbase + q0 + BM - 1 + wr) / kTileN;
+    const int kt_lo = max(0, qbase + q0 - W + 1) / kTileN;
     const int ntiles = kt_hi - kt_lo + 1;
     const bool wave_live = qw0 < N;
 
@@ -729,15 +738,13 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     const int v_lane = v_row * RB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
     const int vq = vswz(v_row);
 
-    auto key_of = [&](int t, int r) __attribute__((always_inline)) { return min((kt_hi - t) * kTileN + r, NK - 1); };
     // copies: wave w fills 1 KiB blocks w, w+8, ... of the tile (lane i
     // writes bytes 16i..16i+15 of a block).  Per block the lane's source is
     // a fixed byte offset inside the tile's 64 rows (K: row sigma(pos),
     // chunk ch; V: the swizzled quarter), so a tile whose rows are 64
-    // consecutive rows of one array costs one scalar base per tile (in band
-    // mode every tile, the last key row bounding the resource).  In chunk
-    // mode other tiles (the diagonal tile at the end, a ring wrap or the
-    // ring/chunk seam) take the general per-row path.
+    // consecutive rows of one array costs one scalar base per tile (band
+    // tiles and chunk tiles, the last key row bounding the resource).  Ring
+    // tiles of chunk mode compute a slot per lane instead (the ring wraps).
     uint32_t koff[NBLK], voff[NBLK];  // row * RB + byte in row; row = off / RB
 #pragma unroll
     for (int it = 0; it < NBLK; ++it) {
@@ -758,26 +765,6 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg, (size_t)N * RB);
     const __amdgpu_buffer_rsrc_t rkr = CHUNK ? make_rsrc(krg, (size_t)p.W * RB) : rk;
     const __amdgpu_buffer_rsrc_t rvr = CHUNK ? make_rsrc(vrg, (size_t)p.W * RB) : rv;
-    // tile t's rows as one run: 0 = gathered rows, 1 = input array at byte
-    // offset soff, 2 = ring at soff
-    auto tile_run = [&](int t, int& soff) __attribute__((always_inline)) {
-        const int j0 = (kt_hi - t) * kTileN;
-        if (j0 + kTileN > NK) return 0;
-        if constexpr (CHUNK) {
-            if (j0 >= qoff) {
-                soff = (j0 - qoff) * RB;
-                return 1;
-            }
-            if (j0 + kTileN <= qoff && hslot0 + j0 + kTileN <= p.W) {
-                soff = (hslot0 + j0) * RB;
-                return 2;
-            }
-            return 0;
-        } else {
-            soff = j0 * RB;
-            return 1;
-        }
-    };
     auto issue_rows = [&](int t, char* dst, const elem_t* src, __amdgpu_buffer_rsrc_t rin,
                           __amdgpu_buffer_rsrc_t rring, const uint32_t* off) __attribute__((always_inline)) {
         if constexpr (!CHUNK) {
@@ -797,40 +784,28 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
                     0);
             return;
         }
-        int soff = 0;
-        const int run = tile_run(t, soff);
-        if (run != 0) {
-            const __amdgpu_buffer_rsrc_t r = run == 1 ? rin : rring;
+        // Chunk mode: a tile is all chunk rows (one scalar base into the
+        // input, rows past the end read as zero) or all ring rows (history
+        // and placeholder keys).  Ring rows take a slot per lane, wrapping at
+        // the ring's end; placeholder rows read history entry 0, which
+        // exists whenever there are placeholders, and are masked.  Source
+        // and offsets are selected, not branched on, so every step issues
+        // the same copies and the copy waits stay partial.
+        const int j0 = (kt_hi - t) * kTileN;
+        const bool ring = j0 < qbase;
+        const int c0 = max(j0 - qbase, 0);
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(src + (size_t)c0 * D, (size_t)(N - c0) * RB);
+        const __amdgpu_buffer_rsrc_t r = ring ? rring : rc;
+        const int s0 = hslot0 + j0 - kmin;  // unwrapped slot of the tile's row 0
 #pragma unroll
-            for (int it = 0; it < NBLK; ++it)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    r, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024), 16, (int)off[it], soff, 0, 0);
-        } else {
-#pragma unroll
-            for (int it = 0; it < NBLK; ++it) {
-                const int row = (int)(off[it] / RB);
-                const int byte = (int)(off[it] % RB);
-                const int j = key_of(t, row);
-                auto* l = (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024);
-                if constexpr (CHUNK) {
-                    // history rows come from the ring, the rest from the chunk
-                    // (lanes on either side load under their own mask: never
-                    // fewer loads than the fixed wait count assumes)
-                    // (the two empty asm statements differ, so that the compiler
-                    // cannot merge the loads into one with a per-lane resource)
-                    if (j < qoff) {
-                        int slot = hslot0 + j;
-                        slot -= slot >= p.W ? p.W : 0;
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rring, l, 16, slot * RB + byte, 0, 0, 0);
-                        asm volatile("; ring rows" ::: "memory");
-                    } else {
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rin, l, 16, (j - qoff) * RB + byte, 0, 0, 0);
-                        asm volatile("; chunk rows" ::: "memory");
-                    }
-                } else {
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rin, l, 16, j * RB + byte, 0, 0, 0);
-                }
-            }
+        for (int it = 0; it < NBLK; ++it) {
+            const int row = (int)(off[it] / RB);
+            const uint32_t byte = off[it] % RB;
+            const uint32_t u = (uint32_t)max(s0 + row, hslot0);  // < 2W
+            const uint32_t slot = min(u, u - (uint32_t)p.W);       // u or u - W
+            const uint32_t o = ring ? slot * RB + byte : off[it];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024), 16, (int)o, 0, 0, 0);
         }
     };
     auto issue_k = [&](int t, char* kl) __attribute__((always_inline)) { issue_rows(t, kl, kg, rk, rkr, koff); };
@@ -867,7 +842,8 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     };
     auto mask_tile = [&](int t, f32x16_t* sc) __attribute__((always_inline)) {
         const int j0 = (kt_hi - t) * kTileN;
-        const bool edge = !(j0 + kTileN - 1 <= qvw0 + wr && j0 >= qvw0 + kQw - W && j0 + kTileN <= NK);
+        const bool edge =
+            !(j0 + kTileN - 1 <= qvw0 + wr && j0 >= qvw0 + kQw - W && j0 + kTileN <= NK && (!CHUNK || j0 >= kmin));
         if (edge) {
             // key of element i in block kb is j0 + 8g + C, C = kb*32 + 16*(i/8) + i%8;
             // with x = qv - j0 - 8g its distance is x - C, so each test is one
@@ -878,11 +854,12 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             int lo = x + wr;           // dist >= -wr  <=>  C <= lo
             int hi = x - W;            // dist < W     <=>  C > hi
             int nk = NK - j0 - 8 * g;  // key < NK     <=>  C < nk
+            if constexpr (CHUNK) hi = max(hi, kmin - 1 - j0 - 8 * g);  // key >= kmin
             asm volatile("" : "+v"(lo), "+v"(hi), "+v"(nk));
             // which bounds this tile can violate (wave-uniform): most edge
             // tiles need one compare per element, not three
             const bool need_lo = j0 + kTileN - 1 > qvw0 + wr, need_nk = j0 + kTileN > NK;
-            const bool need_hi = j0 < qvw0 + kQw - W;
+            const bool need_hi = j0 < qvw0 + kQw - W || (CHUNK && j0 < kmin);
             auto apply = [&](auto keep_of) __attribute__((always_inline)) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
@@ -1017,11 +994,11 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     };
 
     const int n = ntiles;
-    if constexpr (!CHUNK) {
-        // V(0) may end past the last key row; whether or not a range-checked
-        // copy writes its zeros, those rows of vb0 must hold finite values
-        // (they meet P = 0), so the buffer starts zeroed (the barrier below
-        // orders these writes before the copies)
+    {
+        // V(0), the top tile, may end past the last key row; whether or not
+        // a range-checked copy writes its zeros, those rows of vb0 must hold
+        // finite values (they meet P = 0), so the buffer starts zeroed (the
+        // barrier below orders these writes before the copies)
         const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int it = 0; it < TILE_BYTES / (kThreads8 * 16); ++it) *(u32x4_t*)(vb0 + (it * kThreads8 + tid) * 16) = z;

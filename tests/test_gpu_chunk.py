@@ -102,6 +102,10 @@ def test_ring_append_bit_exact(dtype, d, W, T, p0s):
     ("bf16", 128, 8, 64, 200, [3, 64]),                   # chunk longer than the window
     ("bf16", 64, 1, 1, 17, [0, 5]),                       # window 1: each row reads itself only
     ("f32", 64, 2, 1000, 70, [0, 999, 2500]),
+    # 8-wave kernel: d = 64, history lengths not multiples of the 64-key tile
+    ("bf16", 64, 4, 200, 150, [0, 2, 70, 199, 200, 5000]),
+    # 8-wave kernel: the history wraps around the ring's end inside a tile
+    ("bf16", 128, 4, 1000, 130, [0, 999, 1500, 2500]),
 ])
 def test_chunk_prefill_vs_oracle(dtype, d, G, W, T, p0s):
     say(f"chunk_prefill {dtype} d={d} G={G} W={W} T={T} p0={p0s}")
