@@ -106,6 +106,8 @@ def test_ring_append_bit_exact(dtype, d, W, T, p0s):
     ("bf16", 64, 4, 200, 150, [0, 2, 70, 199, 200, 5000]),
     # 8-wave kernel: the history wraps around the ring's end inside a tile
     ("bf16", 128, 4, 1000, 130, [0, 999, 1500, 2500]),
+    # 8-wave kernel: a history of exactly two tiles (no placeholder keys)
+    ("bf16", 128, 4, 129, 100, [128, 129, 1000]),
 ])
 def test_chunk_prefill_vs_oracle(dtype, d, G, W, T, p0s):
     say(f"chunk_prefill {dtype} d={d} G={G} W={W} T={T} p0={p0s}")
