@@ -51,14 +51,15 @@ constexpr int kKeysPerTile = 64;
 // Waves per workgroup of the band kernels, which also picks the kernel (8
 // waves: the 8-wave kernel, 4: the 4-wave one).  Every wave of a workgroup
 // walks the key tiles of all its rows, so a workgroup should span few
-// positions: bf16 band and chunk modes with at least four query heads per KV
-// head run 8 waves (4 heads x 64 positions), everything else (fp32, and the
-// modes with extra keys outside the window) 4 waves.  The 8-wave kernel
+// positions: bf16 band and chunk modes with an even number of query heads
+// per KV head run 8 waves (4 heads x 64 positions, or 2 heads x 128), and
+// everything else (fp32, one query head per KV head, and the modes with
+// extra keys outside the window) 4 waves.  The 8-wave kernel
 // addresses a K/V array with 32-bit byte offsets: `rows` (the longest K/V
 // array of one head, in rows of `d` bf16 values) must stay below 2 GiB.
 inline int waves_per_group(bool bf16, bool keylist, int G, long long rows, int d) {
     const bool small = rows * d * 2 < (1ll << 31);
-    return bf16 && !keylist && G % 4 == 0 && small ? 8 : 4;
+    return bf16 && !keylist && G % 2 == 0 && small ? 8 : 4;
 }
 
 // Split a workgroup's waves into HG query heads (of one KV head) times PB
