@@ -8,11 +8,20 @@ with inputs already resident in HBM.  `value` is the in-band throughput
 allowed-key count (only in-band pairs count; masked work inside edge tiles
 counts against the kernel).  The same line carries:
   * roofline   -- the band kernel against the bf16 dense matrix-core peak,
-                  with HIP-event timing on the launch stream, and the HBM
-                  traffic measured by rocprofv3 counters when the summary in
-                  profiles/ was taken on the current kernel source;
+                  with HIP-event timing on the launch stream (median of the
+                  per-launch events; the mean beside it), the graphics clock
+                  sampled while the timed launches run and the fraction of
+                  the peak scaled to that clock, and the HBM traffic measured
+                  by rocprofv3 counters when the summary in profiles/ was
+                  taken on the current kernel source;
+  * parity     -- max and mean |error| of the timed launch's output against
+                  the float64 oracle's whole output (computed by the
+                  cpu_baseline leg);
   * decode     -- the rolling-window decode step (64 sequences, W=4096 ring,
-                  32/8 heads, d=128) in GB/s of algorithmic bytes vs 8 TB/s;
+                  32/8 heads, d=128) in GB/s of algorithmic bytes vs 8 TB/s,
+                  and the same step for 8 sequences, which splits each
+                  sequence's slots over several workgroups and merges them
+                  (split-K plus the merge kernel);
   * chunk      -- chunked prefill over the rolling cache (4 sequences x 4096
                   new tokens, cached lengths 0 / 1500 / 4095 / 61440) in
                   in-band TFLOP/s, and the ring append of the same chunk;
@@ -24,7 +33,7 @@ counts against the kernel).  The same line carries:
                   HBM-bound (in-band TFLOP/s and GB/s of Q+K+V+O);
   * cpu_baseline -- the float64 oracle on the host cores over the whole
                   prefill workload (run before the GPU is touched, since its
-                  worker pool forks).
+                  worker pool forks), with the host's CPU model.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -44,6 +53,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak
+PEAK_CLOCK_MHZ = 2400.0          # the graphics clock the MFMA peak is quoted at
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "band8_traffic_mistral16k.txt")
 BAND_SOURCES = ["sparse_causal_attention_band_amd/csrc/swa_band_fwd.hip",
                 "sparse_causal_attention_band_amd/csrc/swa_internal.h",
@@ -99,7 +109,21 @@ def read_traffic(workload: str):
         return None
 
 
+def cpu_model() -> str | None:
+    """The host CPU's model name (as lscpu prints it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, q, k, v, rows):
+    """The float64 oracle over the given query rows of every (batch, head).
+    Returns (baseline record, oracle output float64 [B, Hq, len(rows), d])."""
     import numpy as np
 
     import oracle
@@ -109,8 +133,8 @@ def cpu_baseline(cfg, q, k, v, rows):
     ks = k.float().numpy()
     vs = v.float().numpy()
     t0 = time.perf_counter()
-    _, used = oracle.attn_fwd_parallel(qs, ks, vs, cfg.window, cfg.stride, 1 / math.sqrt(cfg.d),
-                                       np.asarray(rows), workers=workers)
+    want, used = oracle.attn_fwd_parallel(qs, ks, vs, cfg.window, cfg.stride, 1 / math.sqrt(cfg.d),
+                                          np.asarray(rows), workers=workers)
     dt = time.perf_counter() - t0
     pairs = 0
     for i in rows:
@@ -118,19 +142,111 @@ def cpu_baseline(cfg, q, k, v, rows):
         if cfg.stride > 0 and i >= cfg.window:
             pairs += (i - cfg.window) // cfg.stride + 1
     flops = 4.0 * cfg.B * cfg.Hq * cfg.d * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
-            "sample": f"query rows {rows[0]}..{rows[-1]} of every (batch, head) of {cfg.name} "
-                      f"({pairs * cfg.B * cfg.Hq:.3e} allowed pairs, float64 numpy, {dt:.2f} s wall)"}
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"query rows {rows[0]}..{rows[-1]} of every (batch, head) of {cfg.name} "
+                     f"({pairs * cfg.B * cfg.Hq:.3e} allowed pairs, float64 numpy, {dt:.2f} s wall)"}
+    return rec, want
 
 
 def decode_cpu_baseline(cfg, q, kr, vr, pos):
+    """The float64 decode oracle over the whole step: (seconds, output)."""
     import oracle
 
     t0 = time.perf_counter()
-    oracle.decode(q.float().numpy(), kr.float().numpy(), vr.float().numpy(), pos.numpy(), cfg.window,
-                  1 / math.sqrt(cfg.d))
+    want = oracle.decode(q.float().numpy(), kr.float().numpy(), vr.float().numpy(), pos.numpy(), cfg.window,
+                         1 / math.sqrt(cfg.d))
     dt = time.perf_counter() - t0
-    return dt
+    return dt, want
+
+
+def abs_error(got, want) -> dict:
+    """max and mean |got - want| over every element (want float64, same
+    shape), taken one leading slice at a time to bound host memory."""
+    import numpy as np
+
+    g = got.detach().float().cpu().numpy()
+    mx, tot, cnt, nonfinite = 0.0, 0.0, 0, 0
+    for a, b in zip(g.reshape(-1, *g.shape[-2:]), want.reshape(-1, *want.shape[-2:])):
+        e = np.abs(a.astype(np.float64) - b)
+        fin = np.isfinite(e)
+        nonfinite += int((~fin).sum())
+        mx = max(mx, float(e[fin].max()) if fin.any() else 0.0)
+        tot += float(e[fin].sum())
+        cnt += e.size
+    return {"max_abs_err": mx, "mean_abs_err": tot / max(1, cnt), "elements": cnt, "nonfinite": nonfinite}
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (MHz) through amdsmi on a background
+    thread while a timed region runs.  Best effort: where the management
+    library is unavailable it records why and reports no clock."""
+
+    def __init__(self, period_s: float = 0.001):
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self._h = None
+        self._stop = None
+        self._thread = None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if not handles:
+                raise RuntimeError("no GPU handle")
+            self._amdsmi = amdsmi
+            self._h = handles[0]
+            self._read()
+        except Exception as e:  # noqa: BLE001 - reported, never fatal
+            self.error = f"{type(e).__name__}: {e}"
+            self._h = None
+
+    def _read(self):
+        a = self._amdsmi
+        try:
+            m = a.amdsmi_get_gpu_metrics_info(self._h)
+            xs = [x for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 10000]
+            if xs:
+                return sum(xs) / len(xs)
+            x = m.get("current_gfxclk")
+            if isinstance(x, (int, float)) and 0 < x < 10000:
+                return float(x)
+        except Exception:  # noqa: BLE001 - fall back to the clock query
+            pass
+        return float(a.amdsmi_get_clock_info(self._h, a.AmdSmiClkType.GFX)["clk"])
+
+    def start(self):
+        import threading
+
+        if self._h is None:
+            return
+        self.samples = []
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self._read())
+                except Exception as e:  # noqa: BLE001
+                    self.error = f"{type(e).__name__}: {e}"
+                    return
+                self._stop.wait(self.period)
+
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+
+    def stop(self) -> dict:
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+            self._thread = None
+        xs = sorted(self.samples)
+        if not xs:
+            return {"sclk_mhz_median": None, "samples": 0, "error": self.error}
+        return {"sclk_mhz_median": xs[len(xs) // 2], "sclk_mhz_min": xs[0], "sclk_mhz_max": xs[-1],
+                "samples": len(xs), "source": "amdsmi gpu metrics (current graphics clock)"}
 
 
 def two_sided_pairs(N: int, left: int, right: int) -> int:
@@ -167,11 +283,11 @@ def variant_legs(swa, inputs, torch, dev, args):
 
     def leg(name, fn, pairs_per_head, maps=1, extra=None):
         per, _ = time_launches(lambda i=0: fn(), steps, warm, torch)
-        ms = sum(per) / len(per)
+        ms = median(per)
         fl = 4.0 * B * Hq * d * pairs_per_head * maps
         res[name] = {"value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                      "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "avg_ms": round(ms, 4), "algorithmic_flops": fl}
+                     "median_ms": round(ms, 4), "algorithmic_flops": fl}
         if extra:
             res[name].update(extra)
 
@@ -200,11 +316,12 @@ def other_prefill_legs(swa, inputs, torch, dev, args):
         out = torch.empty_like(q)
         per, _ = time_launches(lambda i=0: swa.attn_fwd(q, k, v, window=cfg.window, stride=cfg.stride, out=out),
                                steps, 10, torch)
-        ms = sum(per) / len(per)
+        ms = median(per)
         fl = 4.0 * cfg.B * cfg.Hq * cfg.d * allowed_pairs(cfg.N, cfg.window, cfg.stride)
         tf = fl / (ms * 1e-3) / 1e12
         leg = {"value": round(tf, 2), "unit": "TFLOP/s", "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-               "avg_ms": round(ms, 4), "steps": steps, "algorithmic_flops": fl}
+               "median_ms": round(ms, 4), "steps": steps, "algorithmic_flops": fl,
+               "kernel": band_kernel_name(cfg)}
         if cfg.stride:
             # compulsory HBM bytes: Q and O per query head, K and V per KV head
             nb = 2 * (2 * cfg.B * cfg.Hq + 2 * cfg.B * cfg.Hkv) * cfg.N * cfg.d
@@ -216,12 +333,31 @@ def other_prefill_legs(swa, inputs, torch, dev, args):
     return res
 
 
-def time_launches(fn, steps, warmup, torch):
+def band_kernel_name(cfg) -> str:
+    """The band kernel a forward over cfg runs, by the library's routing rule:
+    bf16, no extra keys (stride 0), an even number of query heads per KV head
+    and K/V arrays under 2 GiB per head take the 8-wave kernel."""
+    bf16 = "bfloat16" in str(cfg.dtype)
+    small = cfg.N * cfg.d * 2 < (1 << 31)
+    if bf16 and cfg.stride == 0 and (cfg.Hq // cfg.Hkv) % 2 == 0 and small:
+        return f"band8_kernel<d={cfg.d}, band>"
+    return f"band_fwd_kernel<{'bf16' if bf16 else 'fp32'}, d={cfg.d}, {'strided' if cfg.stride else 'band'}>"
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def time_launches(fn, steps, warmup, torch, on_start=None, on_end=None):
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    if on_start is not None:
+        on_start()
     t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record()
@@ -229,8 +365,45 @@ def time_launches(fn, steps, warmup, torch):
         ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if on_end is not None:
+        on_end()
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     return per, wall
+
+
+def decode_leg(swa, torch, dev, dcfg, dq, dkr, dvr, dpos, steps, warmup, copies, cpu=None):
+    """Time one decode step over `copies` ring copies taken in turn (so no
+    step re-reads a cache-resident ring); GB/s of algorithmic bytes."""
+    B, Hq, Hkv, d, W = dq.shape[0], dcfg.Hq, dcfg.Hkv, dcfg.d, dcfg.window
+    dqd, dposd = dq.to(dev), dpos.to(dev)
+    rings = [(dkr.to(dev), dvr.to(dev)) for _ in range(copies)]
+    dout = torch.empty_like(dqd)
+    need = swa.decode_workspace_bytes(B, Hq, Hkv, d, W)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
+
+    def dstep(i=0):
+        kr_, vr_ = rings[i % copies]
+        swa.decode(dqd, kr_, vr_, dposd, out=dout, workspace=ws)
+
+    dper, _ = time_launches(dstep, steps, warmup, torch)
+    dms = median(dper)
+    n = dpos.clamp(min=0).clamp(max=W).to(torch.int64)
+    dbytes = int(n.sum()) * 2 * Hkv * d * 2 + 2 * B * Hq * d * 2 + 4 * B
+    gbs = dbytes / (dms * 1e-3) / 1e9
+    splits = max(1, need // (B * Hq * (d + 2) * 4)) if need else 1
+    rec = {"sequences": B, "value": round(gbs, 1), "unit": "GB/s", "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+           "median_step_ms": round(dms, 4), "avg_step_ms": round(sum(dper) / len(dper), 4), "steps": steps,
+           "algorithmic_bytes_per_step": dbytes, "splits_per_sequence": splits, "ring_copies": copies,
+           "kernels": f"decode_split_kernel<bf16,{d},{Hq // Hkv}>" +
+                      (" + decode_merge_kernel" if need else " (one split: no merge kernel)")}
+    if cpu is not None:
+        dt, want = cpu
+        rec["parity"] = abs_error(dout, want)
+        rec["cpu_baseline"] = {"value": round(dbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "cpu_model": cpu_model(),
+                               "sample": f"whole {B}-sequence step, float64 numpy, {dt:.2f} s"}
+    del rings, dqd, dposd, dout, ws
+    return rec
 
 
 def main():
@@ -247,6 +420,7 @@ def main():
                     help="skip the two-sided, differential and global-token legs")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the Gemma-shaped and local+strided prefill legs")
+    ap.add_argument("--no-clock", action="store_true", help="do not sample the graphics clock")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -269,14 +443,17 @@ def main():
 
     dcfg = inputs.DECODE
     dq, dkr, dvr, dpos = inputs.decode_inputs(dcfg)
+    SMALL_B = 8
+    sq, skr, svr, spos = inputs.decode_inputs(dcfg, B=SMALL_B)
 
-    cpu = None
-    dec_cpu_s = None
+    cpu = want = None
+    dec_cpu = small_cpu = None
     if not args.no_cpu_baseline:
         rows = list(range(cfg.N))  # the whole workload: every row of every (batch, head)
-        cpu = cpu_baseline(cfg, q, k, v, rows)
+        cpu, want = cpu_baseline(cfg, q, k, v, rows)
         if not args.no_decode:
-            dec_cpu_s = decode_cpu_baseline(dcfg, dq, dkr, dvr, dpos)
+            dec_cpu = decode_cpu_baseline(dcfg, dq, dkr, dvr, dpos)
+            small_cpu = decode_cpu_baseline(dcfg, sq, skr, svr, spos)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -286,15 +463,23 @@ def main():
     def step(i=0):
         swa.attn_fwd(qd, kd, vd, window=cfg.window, stride=cfg.stride, out=out)
 
-    per, wall = time_launches(step, args.steps, args.warmup, torch)
-    ms = sum(per) / len(per)
+    clock = None if args.no_clock else ClockSampler()
+    per, wall = time_launches(step, args.steps, args.warmup, torch,
+                              on_start=clock.start if clock else None, on_end=clock.stop if clock else None)
+    clk = clock.stop() if clock else {"sclk_mhz_median": None, "samples": 0, "error": "not sampled"}
+    ms = median(per)
     value = flops / (ms * 1e-3) / 1e12
     traffic = read_traffic(cfg.name)
     roof = {"bound": "mfma", "achieved": round(value, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-            "kernel": "band8_kernel<d=128, band>" if cfg.Hq // cfg.Hkv % 4 == 0 and cfg.stride == 0
-            else "band_fwd_kernel<bf16, d=%d>" % cfg.d, "avg_launch_ms": round(ms, 4),
-            "algorithmic_flops_per_launch": flops}
+            "kernel": band_kernel_name(cfg), "median_launch_ms": round(ms, 4),
+            "avg_launch_ms": round(sum(per) / len(per), 4), "min_launch_ms": round(min(per), 4),
+            "algorithmic_flops_per_launch": flops,
+            "peak_clock_mhz": PEAK_CLOCK_MHZ, "clock": clk}
+    if clk.get("sclk_mhz_median"):
+        adj = MFMA_BF16_PEAK_TFLOPS * clk["sclk_mhz_median"] / PEAK_CLOCK_MHZ
+        roof["peak_at_observed_clock"] = round(adj, 1)
+        roof["frac_at_observed_clock"] = round(value / adj, 4)
 
     line = {
         "metric": "SWA prefill in-band TFLOP/s (% bf16 MFMA peak); decode GB/s (% HBM peak)",
@@ -314,34 +499,19 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if want is not None:
+        line["parity"] = dict(abs_error(out, want), against="float64 oracle, every output element",
+                              bound_max=1.5e-2, bound_mean=1e-3)
+        del want
+    del qd, kd, vd, out
 
     if not args.no_decode:
-        del qd, kd, vd, out
-        B, Hq, Hkv, d, W = dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.d, dcfg.window
-        dqd, dposd = dq.to(dev), dpos.to(dev)
-        # two ring copies, alternated, so consecutive steps do not re-read a
-        # cache-resident ring
-        rings = [(dkr.to(dev), dvr.to(dev)), (dkr.to(dev), dvr.to(dev))]
-        dout = torch.empty_like(dqd)
-        need = swa.decode_workspace_bytes(B, Hq, Hkv, d, W)
-        ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
-
-        def dstep(i=0):
-            kr_, vr_ = rings[i % 2]
-            swa.decode(dqd, kr_, vr_, dposd, out=dout, workspace=ws)
-
-        dper, dwall = time_launches(dstep, max(args.steps, 20), args.warmup, torch)
-        dms = sum(dper) / len(dper)
-        n = dpos.clamp(min=0).clamp(max=W).to(torch.int64)
-        dbytes = int(n.sum()) * 2 * Hkv * d * 2 + 2 * B * Hq * d * 2 + 4 * B
-        gbs = dbytes / (dms * 1e-3) / 1e9
-        line["decode"] = {"workload": dcfg.name, "value": round(gbs, 1), "unit": "GB/s",
-                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "avg_step_ms": round(dms, 4),
-                          "algorithmic_bytes_per_step": dbytes,
-                          "kernels": "decode_split_kernel<bf16,128,4> (one split: no merge kernel)",
-                          "cpu_baseline": None if dec_cpu_s is None else
-                          {"value": round(dbytes / dec_cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1,
-                           "kind": "oracle", "sample": f"whole {dcfg.name} step, float64 numpy, {dec_cpu_s:.2f} s"}}
+        line["decode"] = dict({"workload": dcfg.name},
+                              **decode_leg(swa, torch, dev, dcfg, dq, dkr, dvr, dpos, max(args.steps, 20),
+                                           args.warmup, 2, dec_cpu))
+        line["decode_split"] = dict({"workload": f"decode_ring4096_b{SMALL_B}"},
+                                    **decode_leg(swa, torch, dev, dcfg, sq, skr, svr, spos, max(args.steps, 20),
+                                                 args.warmup, 4, small_cpu))
 
     if not args.no_chunk:
         ccfg = inputs.CHUNK
@@ -358,15 +528,16 @@ def main():
 
         cper, _ = time_launches(cstep, args.steps, args.warmup, torch)
         aper, _ = time_launches(astep, args.steps, args.warmup, torch)
-        cms, ams = sum(cper) / len(cper), sum(aper) / len(aper)
+        cms, ams = median(cper), median(aper)
         cpairs = sum(min(p + r + 1, ccfg.window) for p in ccfg.p0 for r in range(ccfg.T))
         cflops = 4.0 * ccfg.Hq * ccfg.d * cpairs
         abytes = 2 * 2 * len(ccfg.p0) * ccfg.Hkv * min(ccfg.T, ccfg.window) * ccfg.d * 2  # K,V read + write
         line["chunk"] = {"workload": ccfg.name, "p0": list(ccfg.p0), "value": round(cflops / (cms * 1e-3) / 1e12, 2),
                          "unit": "TFLOP/s", "frac_mfma": round(cflops / (cms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "avg_launch_ms": round(cms, 4), "algorithmic_flops_per_launch": cflops,
+                         "median_launch_ms": round(cms, 4), "avg_launch_ms": round(sum(cper) / len(cper), 4),
+                         "algorithmic_flops_per_launch": cflops,
                          "kernel": "band8_kernel<d=128, chunk>",
-                         "ring_append": {"avg_launch_ms": round(ams, 4), "bytes": abytes,
+                         "ring_append": {"median_launch_ms": round(ams, 4), "bytes": abytes,
                                          "GB_s": round(abytes / (ams * 1e-3) / 1e9, 1)}}
         del cq, ck, cv, ckr, cvr, cp0, cout
 

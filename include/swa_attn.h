@@ -140,9 +140,9 @@ SWA_API int swa_decode_f32(const float* q, const float* kring, const float* vrin
  * Two-sided (bidirectional) band, no causal cut: row i reads keys
  * i-left .. i+right (clipped to [0, N)).  The attention-variants page
  * (概念, 滑动窗口注意力) gives the bidirectional window [i - W/2, i + W/2];
- * the SWA page (§3.1, §3.3) gives [i - w, i + w] with a radius w; separate
- * radii cover both.  right = 0 gives the same result as swa_attn_fwd with
- * window = left + 1.
+ * the explainer page "滑动窗口注意力" (§3.1 band mask, §3.3 example) gives
+ * [i - w, i + w] with a radius w; separate radii cover both.  right = 0
+ * gives the same result as swa_attn_fwd with window = left + 1.
  *   q, out : [B, Hq, N, d]   k, v : [B, Hkv, N, d]   (as swa_attn_fwd)
  *   left, right >= 0 (values >= N act as N - 1); other arguments, layouts,
  *   ownership and errors as swa_attn_fwd.
@@ -178,7 +178,8 @@ SWA_API int swa_diff_attn_fwd_f32(const float* q1, const float* k1, const float*
 
 /*
  * Causal local window plus global tokens (attention-variants page, 稀疏 /
- * 块注意力, Longformer / BigBird; SWA page, 其他 Sparse Attention 模式,
+ * 块注意力, Longformer / BigBird; the interview page "Sliding Window
+ * Attention 和 Sparse Attention 有什么区别", 其他 Sparse Attention 模式,
  * Global Token): a few global positions attend to every earlier position
  * and every later position attends to them; the rest keep the window.  Row
  * i reads key j iff j <= i and (i - j < window, or j is global, or i is

@@ -30,9 +30,10 @@ Everything here is the plain definition, written out in float64 with numpy:
   the chunk is written into the ring.
 * The two-sided (bidirectional) band drops the causal cut: row i reads keys
   i-left .. i+right, clipped to the sequence.  The attention-variants page
-  (概念, 滑动窗口注意力) gives [i - W/2, i + W/2]; the SWA page (§3.1 and its
-  §3.3 example) gives [i - w, i + w] with a radius w and builds the mask as
-  start = max(0, i-w), end = min(n, i+w+1).  Separate left and right radii
+  (概念, 滑动窗口注意力) gives [i - W/2, i + W/2]; the explainer page
+  "滑动窗口注意力" (§3.1 band mask and its §3.3 example) gives [i - w, i + w]
+  with a radius w and builds the mask as start = max(0, i-w),
+  end = min(n, i+w+1).  Separate left and right radii
   cover both; right = 0 is the causal band with W = left + 1.
 
 * Differential attention (attention-variants page, 概念 and 第 4 步): two
@@ -41,7 +42,8 @@ Everything here is the plain definition, written out in float64 with numpy:
   band; with W >= N this is the page's causal version.
 
 * Local + global tokens (attention-variants page, 稀疏 / 块注意力, Longformer /
-  BigBird; SWA page, 其他 Sparse Attention 模式, Global Token): a few global
+  BigBird; the interview page "Sliding Window Attention 和 Sparse Attention
+  有什么区别", 其他 Sparse Attention 模式, Global Token): a few global
   positions attend to every position and are attended to by every position,
   the rest keep the local window.  In the causal setting of this library
   "every position" means every position not after the row: row i may read

@@ -268,6 +268,8 @@ def decode(q: torch.Tensor, kring: torch.Tensor, vring: torch.Tensor, pos: torch
     W = kring.shape[2]
     if kring.shape[0] != B or kring.shape[3] != d:
         raise ValueError("ring shape does not match q")
+    if out is not None and (not isinstance(out, torch.Tensor) or out.shape != q.shape):
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}")
     dtype, dev = q.dtype, q.device
     if dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("q must be bfloat16 or float32")

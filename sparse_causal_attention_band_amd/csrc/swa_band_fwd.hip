@@ -13,11 +13,11 @@
 // enumerates only key tiles that meet the band.
 //
 // Two kernels share the tile enumeration, layouts, masking and softmax: the
-// 8-wave bf16 kernel at the end of this file (band and chunk modes with at
-// least four query heads per KV head) and the 4-wave kernel described here
-// (fp32, the strided and global modes, fewer grouped heads, and K/V arrays
-// of 2 GiB or more per head, which the 8-wave kernel's 32-bit byte offsets
-// cannot address).
+// 8-wave bf16 kernel at the end of this file (band and chunk modes with an
+// even number of query heads per KV head) and the 4-wave kernel described
+// here (fp32, the strided and global modes, one or an odd number of query
+// heads per KV head, and K/V arrays of 2 GiB or more per head, which the
+// 8-wave kernel's 32-bit byte offsets cannot address).
 //
 // Structure of the 4-wave kernel (one workgroup = 4 waves = 256 threads):
 //  * A workgroup owns 4 blocks of 32 queries: HG query heads that share one

@@ -31,7 +31,7 @@ struct PrefillParams {
     int neg;      // scale < 0: queries enter with flipped sign (exact)
     int G;        // Hq / Hkv
     int HG;       // query heads of one KV head that share a workgroup
-    int PB;       // 32-query blocks per head in a workgroup (HG * PB == 4)
+    int PB;       // 32-query blocks per head in a workgroup (HG * PB = waves: 4 or 8)
     int nqb;      // query tiles per head
     int ngroups;  // G / HG
     int total;    // workgroups in the grid

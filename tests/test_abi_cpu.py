@@ -105,6 +105,17 @@ def test_python_wrapper_refuses_host_tensors():
         swa.attn_fwd(q.half(), q.half(), q.half(), window=4)
 
 
+def test_python_decode_refuses_a_wrong_shaped_out():
+    """The decode kernel writes B * Hq * d elements into out: a smaller (or
+    differently shaped) out is refused before any device work."""
+    q = torch.zeros(2, 8, 64)
+    ring = torch.zeros(2, 2, 16, 64)
+    pos = torch.ones(2, dtype=torch.int32)
+    for bad in (torch.zeros(2, 8, 32), torch.zeros(1, 8, 64), torch.zeros(2 * 8 * 64)):
+        with pytest.raises(ValueError, match="out must have"):
+            swa.decode(q, ring, ring, pos, out=bad)
+
+
 def test_inputs_are_seeded_and_shaped():
     a = inputs.prefill_inputs(inputs.STRIDED, N=100)
     b = inputs.prefill_inputs(inputs.STRIDED, N=100)

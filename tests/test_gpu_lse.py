@@ -20,6 +20,8 @@ import oracle
 import sparse_causal_attention_band_amd as swa
 from sparse_causal_attention_band_amd import inputs
 
+import full_parity
+
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
@@ -44,8 +46,8 @@ def f64(t):
     return t.detach().cpu().double().numpy()
 
 
-# (B, Hq, Hkv, N, d, W, stride): 8-wave band kernel (Hq/Hkv = 4, 8), 4-wave
-# kernel (1, 2 heads per KV head, strided), ragged ends and W >= N
+# (B, Hq, Hkv, N, d, W, stride): 8-wave band kernel (Hq/Hkv = 2, 4, 8), 4-wave
+# kernel (one head per KV head, strided), ragged ends and W >= N
 SHAPES = [(1, 8, 2, 300, 128, 100, 0), (2, 8, 1, 257, 128, 64, 0), (1, 4, 4, 200, 64, 33, 0),
           (1, 4, 2, 513, 128, 200, 0), (1, 2, 2, 260, 64, 20, 16), (1, 8, 2, 100, 64, 500, 0),
           (1, 16, 2, 129, 128, 1, 0)]
@@ -71,31 +73,27 @@ def test_band_lse_matches_oracle(shape, dt):
 
 
 def test_band_lse_negative_scale_and_mistral_rows():
-    """A negative scale (the sign enters through q), and sampled rows of the
-    Mistral-shaped workload in the launch configuration the bench times."""
+    """A negative scale (the sign enters through q), and every row of the
+    Mistral-shaped workload in the launch configuration the bench times,
+    against the oracle's log-sum-exp (one head per task on the host's cores)."""
     say("band lse negative scale")
     q, k, v = inputs.random_qkv(1, 8, 2, 300, 128, torch.bfloat16, seed=3)
     out, lse = swa.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), window=77, scale=-0.09, return_lse=True)
     torch.cuda.synchronize()
     assert np.abs(f64(lse) - oracle.attn_lse(f64(q), f64(k), 77, 0, -0.09)).max() <= TOL[torch.bfloat16]
-    say("band lse mistral sampled rows")
+    say("band lse mistral, every row")
     cfg = inputs.MISTRAL
     q, k, v = inputs.prefill_inputs(cfg)
     out, lse = swa.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), window=cfg.window, return_lse=True)
     torch.cuda.synchronize()
     lse = f64(lse)
-    rng = np.random.default_rng(0)
-    rows = sorted(set([0, 1, 63, 64, 4095, 4096, cfg.N - 1] + rng.integers(0, cfg.N, 10).tolist()))
-    scale = 1 / math.sqrt(cfg.d)
-    for h in (0, 5, 31):
-        qh = f64(q[:, h:h + 1, :, :])
-        kh = f64(k[:, h // (cfg.Hq // cfg.Hkv):h // (cfg.Hq // cfg.Hkv) + 1, :, :])
-        for i in rows:
-            lo = max(0, i - cfg.window + 1)
-            s = scale * (kh[0, 0, lo:i + 1] @ qh[0, 0, i])
-            m = s.max()
-            want = m + math.log(np.exp(s - m).sum())
-            assert abs(lse[0, h, i] - want) <= TOL[torch.bfloat16], (h, i)
+    qf, kf = q.float().numpy(), k.float().numpy()
+    G, scale = cfg.Hq // cfg.Hkv, 1 / math.sqrt(cfg.d)
+    st = full_parity.compare_heads(
+        [(0, h) for h in range(cfg.Hq)], lambda bh: lse[0, bh[1]],
+        lambda bh: oracle.attn_lse(qf[:, bh[1]:bh[1] + 1], kf[:, bh[1] // G:bh[1] // G + 1], cfg.window, 0,
+                                   scale)[0, 0], tol=TOL[torch.bfloat16])
+    assert st.nonfinite == 0 and st.over == 0, (st.max_err, st.worst)
 
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])

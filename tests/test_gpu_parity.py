@@ -15,6 +15,9 @@ import torch
 import oracle
 import sparse_causal_attention_band_amd as swa
 from sparse_causal_attention_band_amd import inputs
+from tolerances import bf16_element_bound, bf16_mean_bound
+
+import full_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -48,22 +51,22 @@ def check_f32(got, want, what=""):
 def check_bf16(got, want, what="", rounding_term=False):
     """max |err| <= 1.5e-2 and mean |err| <= 1e-3.
 
-    With rounding_term=True (small-window sweeps, whose outputs can exceed 2
-    in magnitude) each element may also differ by the half-ulp of bf16 at
-    |want|: rounding the exact value to the bf16 output already costs that
-    much (2^-6 at |want| in [4, 8)), so a flat 1.5e-2 cannot be met there by
-    any bf16-output kernel.  The five configured workloads use the flat bound.
+    With rounding_term=True (small-window sweeps, whose outputs are
+    near-copies of V rows and can reach 4 in magnitude) an element whose
+    exact value is 4 or more may differ by its bf16 half ulp plus the flat
+    bound's arithmetic share, and the mean bound applies to the error in
+    excess of rounding the exact values once to bf16 (tests/tolerances.py):
+    that rounding alone costs 2^-6 per element from 4 on and ~9.5e-4 on
+    average for one- and two-key rows.  The configured workloads use the
+    flat bounds.
     """
     g = f64(got)
     err = np.abs(g - want)
     assert np.isfinite(g).all(), what
-    tol = np.full(want.shape, 1.5e-2)
-    if rounding_term:
-        e = np.floor(np.log2(np.maximum(np.abs(want), 2.0 ** -126)))
-        half_ulp = 2.0 ** (e - 8)
-        tol = np.maximum(tol, half_ulp + 8e-3)
+    tol = bf16_element_bound(want) if rounding_term else np.full(want.shape, 1.5e-2)
+    mean_tol = bf16_mean_bound(want) if rounding_term else 1e-3
     bad = err > tol
-    assert not bad.any() and err.mean() <= 1e-3, (
+    assert not bad.any() and err.mean() <= mean_tol, (
         f"{what}: max {err.max():.3e} mean {err.mean():.3e}; {int(bad.sum())} elements over tolerance")
 
 
@@ -134,6 +137,9 @@ def test_tiny_config_fp32():
 SHAPES = [  # (B, Hq, Hkv, N, d)
     (1, 1, 1, 1, 64), (1, 2, 1, 7, 64), (2, 4, 2, 63, 128), (1, 4, 1, 65, 64), (1, 8, 2, 200, 128),
     (1, 3, 3, 257, 64), (2, 6, 2, 130, 128), (1, 2, 2, 129, 64),
+    # even head groups of more than one 8-wave workgroup: 6 per KV head (three
+    # groups of 2 heads x 128 positions) and 16 (two groups of 8 heads x 32)
+    (1, 12, 2, 300, 64), (1, 12, 2, 290, 128), (1, 16, 1, 280, 128), (2, 32, 2, 260, 64),
 ]
 
 
@@ -265,29 +271,29 @@ def test_strided_config_full_parity():
     check_bf16(out, want, cfg.name)
 
 
-def _sample_rows(cfg, n_rand=24, seed=0):
-    rng = np.random.default_rng(seed)
-    N, W = cfg.N, cfg.window
-    fixed = [0, 1, 31, 32, 63, 64, W - 2, W - 1, W, W + 1, W + 63, N // 2, N - 65, N - 2, N - 1]
-    rows = []
-    for t, i in enumerate(fixed + list(rng.integers(0, N, n_rand))):
-        b = int(rng.integers(0, cfg.B))
-        h = int(rng.integers(0, cfg.Hq)) if t % 3 else (t % cfg.Hq)
-        rows.append((b, h, int(i)))
-    return rows
-
-
 @pytest.mark.parametrize("cfg", [inputs.MISTRAL, inputs.GEMMA], ids=lambda c: c.name)
-def test_large_config_sampled_parity(cfg):
-    say(cfg.name)
+def test_large_config_full_parity(cfg):
+    """Every output element of the Mistral- and Gemma-shaped workloads, in
+    the launch configuration the benchmark times, against the float64
+    oracle (one (batch, head) per task on the host's cores).  The output
+    buffer starts as NaN, so a row the kernels never write fails."""
+    say(f"{cfg.name} (whole output)")
     q, k, v = inputs.prefill_inputs(cfg)
-    out = run_fwd(q, k, v, cfg.window, cfg.stride)
-    assert bool(torch.isfinite(out.float()).all())
-    picks = _sample_rows(cfg)
-    want = oracle.attn_fwd_rows(q.float().numpy(), k.float().numpy(), v.float().numpy(),
-                                cfg.window, cfg.stride, 1 / math.sqrt(cfg.d), picks)
-    got = torch.stack([out[b, h, i] for b, h, i in picks]).cpu()
-    check_bf16(got, want, cfg.name)
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
+    swa.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), window=cfg.window, stride=cfg.stride, out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    del out
+    qf, kf, vf = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    G, scale = cfg.Hq // cfg.Hkv, 1 / math.sqrt(cfg.d)
+    st = full_parity.compare_heads(
+        [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)],
+        lambda bh: got[bh[0], bh[1]],
+        lambda bh: oracle.attn_fwd(qf[bh[0]:bh[0] + 1, bh[1]:bh[1] + 1], kf[bh[0]:bh[0] + 1, bh[1] // G:bh[1] // G + 1],
+                                   vf[bh[0]:bh[0] + 1, bh[1] // G:bh[1] // G + 1], cfg.window, cfg.stride,
+                                   scale)[0, 0])
+    print(f"{cfg.name}: {st.count} elements, max |err| {st.max_err:.3e}, mean {st.mean_err:.3e}", flush=True)
+    full_parity.assert_bf16(st, cfg.name)
 
 
 # ---------------------------------------------------------------- decode

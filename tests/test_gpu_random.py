@@ -4,10 +4,13 @@ differential attention and chunked prefill over a ring, with ragged
 sequence lengths, group sizes 1..8, head dims 64 and 128, fp32 and bf16.
 Each case prints its parameters before it touches the GPU.
 
-Tolerances as in the other parity tests: fp32 max |err| <= 1e-5; bf16 max
-|err| <= 1.5e-2 and mean |err| <= 1e-3, where an element may also differ by
-the bf16 half-ulp of the exact value plus 8e-3 (outputs of small windows can
-exceed 4 in magnitude, where rounding the exact value alone costs 2^-7).
+Tolerances as in the other parity tests (tests/tolerances.py): fp32 max
+|err| <= 1e-5; bf16 max |err| <= 1.5e-2 and mean |err| <= 1e-3, except that
+small windows return near-copies of V rows, where rounding the exact value
+to bf16 alone costs 2^-6 per element of magnitude 4 or more and ~1e-3 on
+average: an element there may differ by its half ulp plus the flat bound's
+arithmetic share, and the mean bound applies to the error in excess of that
+rounding.
 """
 import math
 import sys
@@ -18,6 +21,7 @@ import torch
 
 import oracle
 import sparse_causal_attention_band_amd as swa
+from tolerances import F32_MAX, bf16_element_bound, bf16_mean_bound
 from sparse_causal_attention_band_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -50,13 +54,11 @@ def check(got, want, dtype, what):
     assert np.isfinite(g).all(), what
     err = np.abs(g - want)
     if dtype == torch.float32:
-        assert err.max() <= 1e-5, f"{what}: max err {err.max():.3e}"
+        assert err.max() <= F32_MAX, f"{what}: max err {err.max():.3e}"
         return
-    e = np.floor(np.log2(np.maximum(np.abs(want), 2.0 ** -126)))
-    tol = np.maximum(1.5e-2, 2.0 ** (e - 8) + 8e-3)
-    worst = np.max(err - tol)
+    worst = np.max(err - bf16_element_bound(want))
     assert worst <= 0, f"{what}: max err {err.max():.3e} (over the bound by {worst:.3e})"
-    assert err.mean() <= 1e-3, f"{what}: mean err {err.mean():.3e}"
+    assert err.mean() <= bf16_mean_bound(want), f"{what}: mean err {err.mean():.3e}"
 
 
 def draw(i):

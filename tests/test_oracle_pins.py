@@ -490,7 +490,7 @@ def test_planted_mistakes_are_caught(monkeypatch):
 
 # ---------------------------------------------------------------- two-sided band
 def _page_two_sided_mask(n, w):
-    """The SWA page's §3.3 construction, restated: ones, then zero the
+    """The explainer page's ("滑动窗口注意力") §3.3 construction, restated: ones, then zero the
     columns before max(0, i-w) and from min(n, i+w+1) on, row by row."""
     m = np.ones((n, n))
     for i in range(n):
