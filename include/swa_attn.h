@@ -273,6 +273,28 @@ SWA_API int swa_ring_append_f32(const float* k, const float* v, const int32_t* p
    for these sizes has one split, and for invalid sizes). */
 SWA_API size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window);
 
+/*
+ * swa_decode (bf16) without a caller-supplied workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops
+ * that must not call the allocator, harnesses that forbid it.  The split
+ * partials go to a scratch array of SWA_DECODE_NOALLOC_SCRATCH_BYTES that the
+ * library holds in each GPU's memory for the life of the process (one copy
+ * per device, located once per device on the first call there).
+ *   Arguments, layouts, results and errors as swa_decode, minus the
+ *   workspace.  Every supported size fits (Hq / Hkv <= 8 and d <= 128 bound
+ *   the split plan's partials below the scratch size); a size that would not
+ *   is refused with SWA_ERR_UNSUPPORTED.  Nothing is allocated: no hipMalloc,
+ *   no hipFree.  The scratch needs no clearing: every partial the merge reads
+ *   is written earlier in the same call.
+ *   All calls on one GPU share that GPU's scratch, which keeps the last call's
+ *   partials: calls that may overlap on one GPU (different streams, or one
+ *   stream and a graph replay) race and must be serialised by the caller.
+ */
+#define SWA_DECODE_NOALLOC_SCRATCH_BYTES 4259840
+SWA_API int swa_decode_noalloc(const void* q, const void* kring, const void* vring, const int32_t* pos,
+                               void* out, int B, int Hq, int Hkv, int d, float scale, int window,
+                               hipStream_t stream);
+
 /* Message for the last non-zero return on the calling thread ("" if none). */
 SWA_API const char* swa_last_error(void);
 

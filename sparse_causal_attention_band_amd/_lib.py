@@ -48,6 +48,7 @@ SIGNATURES = {
     "swa_ring_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "swa_ring_append_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "swa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "swa_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "swa_last_error": (ctypes.c_char_p, []),
 }
 
@@ -295,6 +296,41 @@ def decode(q: torch.Tensor, kring: torch.Tensor, vring: torch.Tensor, pos: torch
     fn = lib().swa_decode if dtype == torch.bfloat16 else lib().swa_decode_f32
     _check(fn(q.data_ptr(), kring.data_ptr(), vring.data_ptr(), pos.data_ptr(), out.data_ptr(),
               B, Hq, kring.shape[1], d, float(scale), ws_ptr, ws_bytes, W, _stream(dev)))
+    return out
+
+
+def decode_noalloc(q: torch.Tensor, kring: torch.Tensor, vring: torch.Tensor, pos: torch.Tensor,
+                   scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """``decode`` (bf16) through the entry point that allocates nothing: the
+    split partials live in the library's per-device scratch, shared by every
+    call on that GPU (calls that may overlap on one GPU race).  ``out`` must
+    be given by callers that cannot allocate; when it is None it is
+    allocated here, as in the other wrappers."""
+    if q.dim() != 3 or kring.dim() != 4 or vring.shape != kring.shape:
+        raise ValueError("q must be [B, Hq, d] and kring/vring [B, Hkv, W, d]")
+    B, Hq, d = q.shape
+    W = kring.shape[2]
+    if kring.shape[0] != B or kring.shape[3] != d:
+        raise ValueError("ring shape does not match q")
+    if out is not None and (not isinstance(out, torch.Tensor) or out.shape != q.shape):
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}")
+    dev = q.device
+    if q.dtype != torch.bfloat16:
+        raise TypeError("decode_noalloc takes bfloat16 tensors")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    for t, n in ((q, "q"), (kring, "kring"), (vring, "vring")):
+        _need(t, n, torch.bfloat16, dev)
+    _need(pos, "pos", torch.int32, dev)
+    if pos.shape != (B,):
+        raise ValueError("pos must be [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(lib().swa_decode_noalloc(q.data_ptr(), kring.data_ptr(), vring.data_ptr(), pos.data_ptr(),
+                                    out.data_ptr(), B, Hq, kring.shape[1], d, float(scale), W, _stream(dev)))
     return out
 
 

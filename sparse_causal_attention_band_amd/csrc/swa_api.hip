@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <mutex>
 #include <string>
 
 #include "swa_attn.h"
@@ -288,10 +289,54 @@ int ring_append(bool bf16, const void* k, const void* v, const int32_t* p0, void
     return ok();
 }
 
+// Scratch of the allocation-free decode entry point: the split partials
+// ([B, Hq, nsplit, d] sums, then [B, Hq, nsplit, 2] (max, sum)).  The split
+// plan splits only below 512 (sequence, KV head) pairs, so pairs x splits
+// stays under 1024 and the partials under 8 heads per KV head x 1022 x
+// (128 + 2) floats.  Each GPU holds its own copy; host code never names the
+// array itself (on the host the name is only a handle), it uses the device
+// address looked up once per device.
+constexpr size_t kNoAllocScratchBytes = SWA_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call there, with that device current); nullptr with an error on failure.
+void* scratch_on_current_device(const char* name, int* rc) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *rc = fail(SWA_ERR_HIP, "%s: hipGetDevice failed: %s", name, hipGetErrorString(e));
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        *rc = fail(SWA_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library tracks", name, dev, kMaxDevices);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) {
+            *rc = fail(SWA_ERR_HIP, "%s: scratch address lookup failed on device %d: %s", name, dev,
+                       hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+// Decode step.  With use_scratch the workspace arguments are ignored and the
+// split partials go to this device's copy of `scratch` (allocation-free
+// entry point).
 int decode(bool bf16, const void* q, const void* kring, const void* vring, const int32_t* pos, void* out, int B,
            int Hq, int Hkv, int d, float scale, void* workspace, size_t workspace_bytes, int window,
-           hipStream_t stream) {
-    const char* name = bf16 ? "swa_decode" : "swa_decode_f32";
+           hipStream_t stream, const char* name = nullptr, bool use_scratch = false) {
+    if (name == nullptr) name = bf16 ? "swa_decode" : "swa_decode_f32";
     if (B < 1 || Hq < 1 || Hkv < 1)
         return fail(SWA_ERR_INVALID_ARG, "%s: B, Hq, Hkv must be >= 1 (B=%d Hq=%d Hkv=%d)", name, B, Hq, Hkv);
     if (Hq % Hkv != 0) return fail(SWA_ERR_INVALID_ARG, "%s: Hq (%d) must be a multiple of Hkv (%d)", name, Hq, Hkv);
@@ -305,6 +350,19 @@ int decode(bool bf16, const void* q, const void* kring, const void* vring, const
     if (pos == nullptr || ((uintptr_t)pos & 3u)) return fail(SWA_ERR_INVALID_ARG, "%s: pos must be non-null, 4-byte aligned", name);
     if (int rc = check_scale(name, scale)) return rc;
     const size_t need = swa::decode_workspace_bytes(B, Hq, Hkv, window, d);
+    if (use_scratch) {
+        if (need > kNoAllocScratchBytes)
+            return fail(SWA_ERR_UNSUPPORTED, "%s: the split partials need %zu bytes, above the %zu-byte scratch",
+                        name, need, kNoAllocScratchBytes);
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need > 0) {
+            int rc = SWA_OK;
+            workspace = scratch_on_current_device(name, &rc);
+            if (workspace == nullptr) return rc;
+            workspace_bytes = kNoAllocScratchBytes;
+        }
+    }
     if (need > 0 && !aligned16(workspace))
         return fail(SWA_ERR_INVALID_ARG, "%s: workspace must be non-null and 16-byte aligned", name);
     if (workspace_bytes < need)
@@ -444,6 +502,12 @@ int swa_ring_append(const void* k, const void* v, const int32_t* p0, void* kring
 int swa_ring_append_f32(const float* k, const float* v, const int32_t* p0, float* kring, float* vring, int B, int Hkv,
                         int T, int d, int window, hipStream_t stream) {
     return ring_append(false, k, v, p0, kring, vring, B, Hkv, T, d, window, stream);
+}
+
+int swa_decode_noalloc(const void* q, const void* kring, const void* vring, const int32_t* pos, void* out, int B,
+                       int Hq, int Hkv, int d, float scale, int window, hipStream_t stream) {
+    return decode(true, q, kring, vring, pos, out, B, Hq, Hkv, d, scale, nullptr, 0, window, stream,
+                  "swa_decode_noalloc", true);
 }
 
 size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int window) {

@@ -105,6 +105,35 @@ def test_python_wrapper_refuses_host_tensors():
         swa.attn_fwd(q.half(), q.half(), q.half(), window=4)
 
 
+def test_noalloc_decode_refuses_bad_arguments_before_launch():
+    L = swa.lib()
+    assert L.swa_decode_noalloc(A, A * 2, A * 3, A * 4, A * 5, 2, 6, 2, 128, 0.1, 64, None) == -2   # 3 heads per KV head
+    assert L.swa_decode_noalloc(A, A * 2, A * 3, A * 4, A * 5, 2, 8, 2, 96, 0.1, 64, None) == -2    # d = 96
+    assert L.swa_decode_noalloc(A, A * 2, A * 3, None, A * 5, 2, 8, 2, 128, 0.1, 64, None) == -1    # pos
+    assert L.swa_decode_noalloc(A, A * 2, A * 3, A * 4, A * 5, 0, 8, 2, 128, 0.1, 64, None) == -1    # B
+    assert L.swa_decode_noalloc(A + 2, A * 2, A * 3, A * 4, A * 5, 2, 8, 2, 128, 0.1, 64, None) == -1  # q aligned
+    assert L.swa_decode_noalloc(A, A * 2, A * 3, A * 4, A * 5, 2, 8, 2, 128, 0.0, 64, None) == -1   # scale
+    assert L.swa_last_error().decode().startswith("swa_decode_noalloc")
+
+
+def test_noalloc_scratch_covers_every_split_plan():
+    """The split plan splits only below 512 (sequence, KV head) pairs, so the
+    partials of any supported shape fit the fixed scratch (the largest: 8
+    heads per KV head, d = 128)."""
+    L = swa.lib()
+    text = open(HEADER).read()
+    cap = int(re.search(r"#define SWA_DECODE_NOALLOC_SCRATCH_BYTES (\d+)", text).group(1))
+    worst = 0
+    for pairs in list(range(1, 520)) + [600, 1000, 4096]:
+        for W in (1, 63, 64, 65, 1000, 4096, 131072):
+            worst = max(worst, L.swa_decode_workspace_bytes(pairs, 8 * pairs, pairs, 128, W))
+            for B, Hkv in ((pairs, 1), (1, pairs)):
+                for G in (1, 2, 4, 8):
+                    for d in (64, 128):
+                        assert L.swa_decode_workspace_bytes(B, G * Hkv, Hkv, d, W) <= cap
+    assert 4_000_000 < worst <= cap  # the bound is tight to within a few per cent
+
+
 def test_python_decode_refuses_a_wrong_shaped_out():
     """The decode kernel writes B * Hq * d elements into out: a smaller (or
     differently shaped) out is refused before any device work."""
