@@ -1019,8 +1019,13 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     wait_older_copies();
     lds_barrier();
 
-    // step t: scores of t+1 from kn, P*V of t from vc; K(t+3) -> ki, V(t+2) -> vi
-    auto step = [&](int t, const char* kn, const char* vc, char* ki, char* vi) __attribute__((always_inline)) {
+    // step t: scores of t+1 from kn, P*V of t from vc; K(t+3) -> ki, V(t+2) -> vi.
+    // MASKED: tile t+1 may be an edge tile of this wave (the wave-uniform
+    // test in mask_tile decides); otherwise it is known to be interior for
+    // every wave and the step has no mask code at all.
+    auto step = [&](auto masked, int t, const char* kn, const char* vc, char* ki, char* vi)
+                    __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked)::value;
         issue_k(min(t + 3, n - 1), ki);
         issue_v(min(t + 2, n - 1), vi);
         // K fragments of the next tile's first two regions; its first
@@ -1039,7 +1044,9 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         softmax_head(mx_cur);
         mx_cur = tile_work(std::true_type{}, std::true_type{}, scur, snext, kn, vc, kf0, kf1,
                            [&]() __attribute__((always_inline)) {
-                               if (t + 1 < n) mask_tile(t + 1, snext);
+                               if constexpr (MASKED) {
+                                   if (t + 1 < n) mask_tile(t + 1, snext);
+                               }
                                return tile_max(snext);
                            });
         scur[0] = snext[0];
@@ -1047,14 +1054,44 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         wait_older_copies();
         lds_barrier();
     };
-    for (int t = 0; t < n; t += 3) {
-        // (already true here; stated so that the compiler's own copy
-        // tracking does not lose it at the loop head)
-        wait_older_copies();
-        step(t, kb1, vb0, kb0, vb2);
-        if (t + 1 < n) step(t + 1, kb2, vb1, kb1, vb0);
-        if (t + 2 < n) step(t + 2, kb0, vb2, kb2, vb1);
+    // Tiles t_a .. t_b lie inside the band of every row of the workgroup
+    // (interior for every wave: after the diagonal tiles of its lowest rows,
+    // at or above the window start of its highest rows, whole, and in chunk
+    // mode past the placeholder keys).  Step t masks tile t+1, so steps
+    // [s1, s2), with t_a <= t+1 <= t_b, need no mask.  The steps run in three
+    // segments -- masked, mask-free, masked -- each starting at a multiple
+    // of three, so every segment rotates the static buffers the same way;
+    // the mask-free segment is a whole number of three-step rounds, so its
+    // loop body has no branch at all (at W = 4096 it holds all but ~4 of the
+    // ~66 steps).
+    const int lo_key = qbase + q0 + wr;                // last key of the lowest rows' band
+    const int hi_key = qbase + q0 + kQw * p.PB - W;    // first key of the highest rows' band
+    int t_a = max(max(kt_hi - ((lo_key - (kTileN - 1)) >> 6), kt_hi - ((NK - kTileN) >> 6)), 0);
+    int t_b = min(kt_hi - ((hi_key + kTileN - 1) >> 6), n - 1);
+    if constexpr (CHUNK) t_b = min(t_b, kt_hi - ((kmin + kTileN - 1) >> 6));
+    int s1 = n, s2 = n;
+    if (t_a <= t_b) {
+        s1 = min((max(t_a - 1, 0) + 2) / 3 * 3, n);
+        s2 = s1 + max(0, t_b - s1) / 3 * 3;  // <= t_b < n; the last step's t+1 = s2 <= t_b
     }
+    auto run_masked = [&](int t0, int t1) __attribute__((always_inline)) {
+        for (int t = t0; t < t1; t += 3) {
+            // (already true here; stated so that the compiler's own copy
+            // tracking does not lose it at the loop head)
+            wait_older_copies();
+            step(std::true_type{}, t, kb1, vb0, kb0, vb2);
+            if (t + 1 < t1) step(std::true_type{}, t + 1, kb2, vb1, kb1, vb0);
+            if (t + 2 < t1) step(std::true_type{}, t + 2, kb0, vb2, kb2, vb1);
+        }
+    };
+    run_masked(0, s1);
+    for (int t = s1; t < s2; t += 3) {
+        wait_older_copies();
+        step(std::false_type{}, t, kb1, vb0, kb0, vb2);
+        step(std::false_type{}, t + 1, kb2, vb1, kb1, vb0);
+        step(std::false_type{}, t + 2, kb0, vb2, kb2, vb1);
+    }
+    run_masked(s2, n);
     // no copy may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(0xF70);
 
