@@ -162,10 +162,15 @@ SWA_API int swa_attn_fwd_two_sided_f32(const float* q, const float* k, const flo
  *   q1, q2, out : [B, Hq, N, d]   k1, k2, v : [B, Hkv, N, d]
  *   lam : fp32 [Hq] on the device
  *   window, scale, d, alignment and errors as swa_attn_fwd.
- * Runs as two launches of the band kernel on `stream`: the first writes
- * A1 V to out, the second subtracts lam * A2 V from it in its epilogue (in
- * the bf16 entry point A1 V is therefore rounded to bf16 once before the
- * subtraction).  out must not overlap any input.
+ * bf16 with window < 512 (K/V arrays under 2 GiB per head): one pass of
+ * the band kernel in which each workgroup runs both maps over one tile
+ * stream -- the K tiles of both pairs and the shared V tile are staged once
+ * per step -- and the result A1 V / l1 - lam * A2 V / l2 is formed in fp32
+ * and rounded to bf16 once.  Otherwise (longer windows, where two launches
+ * measure faster; fp32; larger arrays): two launches on `stream`, the first
+ * writing A1 V to out and the second subtracting lam * A2 V in its epilogue
+ * (in bf16, A1 V is then rounded once before the subtraction).  out must
+ * not overlap any input.
  */
 SWA_API int swa_diff_attn_fwd(const void* q1, const void* k1, const void* q2, const void* k2, const void* v,
                               const float* lam, void* out, int B, int Hq, int Hkv, int N, int d, int window,

@@ -634,6 +634,12 @@ __device__ __forceinline__ void lds_barrier() {
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(PrefillParams p) {
     constexpr bool CHUNK = MODE == kChunk;
+    // Differential attention (A1 - lam A2) V in one pass: waves 0..3 run the
+    // first map (q, k) and waves 4..7 the second (q2, k2) for the same four
+    // 32-query blocks, over one tile stream that stages K1, K2 and the
+    // shared V once per step; the epilogue combines the two normalised
+    // results through LDS and rounds once.
+    constexpr bool DIFF = MODE == kDiff;
     using elem_t = uint16_t;
     constexpr int RB = D * 2;                    // bytes per K/V row
     constexpr int CPR = RB / 16;                 // 16-byte chunks per row
@@ -643,7 +649,8 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     constexpr int NQF = D / 16;                  // Q fragments
     static_assert(TILE_BYTES % 8192 == 0, "copy split");
     static_assert(NDB == NQF / 2, "one P*V instruction per score instruction");
-    static_assert(MODE == kBand || MODE == kChunk, "band tiles only: no compact (strided or listed) keys");
+    static_assert(MODE == kBand || MODE == kChunk || MODE == kDiff,
+                  "band tiles only: no compact (strided or listed) keys");
 
     __shared__ __attribute__((aligned(16))) char kb0[TILE_BYTES];
     __shared__ __attribute__((aligned(16))) char kb1[TILE_BYTES];
@@ -651,11 +658,17 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     __shared__ __attribute__((aligned(16))) char vb0[TILE_BYTES];
     __shared__ __attribute__((aligned(16))) char vb1[TILE_BYTES];
     __shared__ __attribute__((aligned(16))) char vb2[TILE_BYTES];
+    // the second map's K buffers (differential attention only)
+    __shared__ __attribute__((aligned(16))) char kc0[DIFF ? TILE_BYTES : 16];
+    __shared__ __attribute__((aligned(16))) char kc1[DIFF ? TILE_BYTES : 16];
+    __shared__ __attribute__((aligned(16))) char kc2[DIFF ? TILE_BYTES : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS copy targets stay scalar
     const int g = lane >> 5, l32 = lane & 31;
+    const int map = DIFF ? (wave >> 2) : 0;   // which attention map this wave computes
+    const int wv = DIFF ? (wave & 3) : wave;  // the wave's query block within its map
 
     const int L = xcd_remap(blockIdx.x, p.total);
     const int qb = L % p.nqb;
@@ -685,8 +698,8 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     const int W = min(p.W, NK);
     const int BM = kQw * p.PB;
     const int q0 = qb * BM;
-    const int h = kvh * p.G + hg * p.HG + (wave % p.HG);
-    const int qw0 = q0 + kQw * (wave / p.HG);
+    const int h = kvh * p.G + hg * p.HG + (wv % p.HG);
+    const int qw0 = q0 + kQw * (wv / p.HG);
     const int qi = qw0 + l32;
     const int qv = qbase + qi;
     const int qvw0 = qbase + qw0;
@@ -694,8 +707,9 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     const size_t kv_head = (size_t)(b * p.Hkv + kvh) * (size_t)N * D;
     const size_t q_head = (size_t)(b * p.Hq + h) * (size_t)N * D;
     const elem_t* kg = (const elem_t*)p.k + kv_head;
+    const elem_t* k2g = DIFF ? (const elem_t*)p.k2 + kv_head : kg;
     const elem_t* vg = (const elem_t*)p.v + kv_head;
-    const elem_t* qg = (const elem_t*)p.q + q_head;
+    const elem_t* qg = (const elem_t*)(map ? p.q2 : p.q) + q_head;
     elem_t* og = (elem_t*)p.out + q_head;
     const size_t ring_head = (size_t)(b * p.Hkv + kvh) * (size_t)p.W * D;
     const elem_t* krg = CHUNK ? (const elem_t*)p.kring + ring_head : nullptr;
@@ -808,12 +822,16 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
                 r, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024), 16, (int)o, 0, 0, 0);
         }
     };
-    auto issue_k = [&](int t, char* kl) __attribute__((always_inline)) { issue_rows(t, kl, kg, rk, rkr, koff); };
+    auto issue_k = [&](int t, char* kl, char* kl2) __attribute__((always_inline)) {
+        issue_rows(t, kl, kg, rk, rkr, koff);
+        if constexpr (DIFF) issue_rows(t, kl2, k2g, rk, rk, koff);
+    };
     auto issue_v = [&](int t, char* vl) __attribute__((always_inline)) { issue_rows(t, vl, vg, rv, rvr, voff); };
     // Every step issues the same copies (past the end of the list the last
     // tile again, into a buffer nobody reads any more), so one fixed wait
-    // count holds: the 2*NBLK loads of the current step may stay in flight.
-    auto wait_older_copies = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0xF70 | (2 * NBLK)); };
+    // count holds: the CPS*NBLK loads of the current step may stay in flight.
+    constexpr int CPS = DIFF ? 3 : 2;  // tiles copied per step: K (K1 and K2) and V
+    auto wait_older_copies = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0xF70 | (CPS * NBLK)); };
 
     f32x16_t oacc[NDB];
 #pragma unroll
@@ -1004,17 +1022,17 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         for (int it = 0; it < TILE_BYTES / (kThreads8 * 16); ++it) *(u32x4_t*)(vb0 + (it * kThreads8 + tid) * 16) = z;
     }
     // prologue: K(0), scores of tile 0; then K(1), V(0), K(2), V(1) in flight
-    issue_k(0, kb0);
+    issue_k(0, kb0, kc0);
     __builtin_amdgcn_s_waitcnt(0xF70);
     lds_barrier();
     f32x16_t scur[2];
-    scores(kb0, scur);
+    scores(map ? kc0 : kb0, scur);
     mask_tile(0, scur);
     float mx_cur = tile_max(scur);
     lds_barrier();  // tile 0's K reads are done before K(3) lands in kb0
-    issue_k(min(1, n - 1), kb1);
+    issue_k(min(1, n - 1), kb1, kc1);
     issue_v(0, vb0);
-    issue_k(min(2, n - 1), kb2);
+    issue_k(min(2, n - 1), kb2, kc2);
     issue_v(min(1, n - 1), vb1);
     wait_older_copies();
     lds_barrier();
@@ -1023,11 +1041,13 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     // MASKED: tile t+1 may be an edge tile of this wave (the wave-uniform
     // test in mask_tile decides); otherwise it is known to be interior for
     // every wave and the step has no mask code at all.
-    auto step = [&](auto masked, int t, const char* kn, const char* vc, char* ki, char* vi)
-                    __attribute__((always_inline)) {
+    // kn2, ki2: the second map's K buffers (differential attention)
+    auto step = [&](auto masked, int t, const char* kn1, const char* kn2, const char* vc, char* ki, char* ki2,
+                    char* vi) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked)::value;
-        issue_k(min(t + 3, n - 1), ki);
+        issue_k(min(t + 3, n - 1), ki, ki2);
         issue_v(min(t + 2, n - 1), vi);
+        const char* kn = map ? kn2 : kn1;  // this wave's K buffer
         // K fragments of the next tile's first two regions; its first
         // region's scores, then this tile's head (row maximum taken in the
         // previous step)
@@ -1079,27 +1099,52 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             // (already true here; stated so that the compiler's own copy
             // tracking does not lose it at the loop head)
             wait_older_copies();
-            step(std::true_type{}, t, kb1, vb0, kb0, vb2);
-            if (t + 1 < t1) step(std::true_type{}, t + 1, kb2, vb1, kb1, vb0);
-            if (t + 2 < t1) step(std::true_type{}, t + 2, kb0, vb2, kb2, vb1);
+            step(std::true_type{}, t, kb1, kc1, vb0, kb0, kc0, vb2);
+            if (t + 1 < t1) step(std::true_type{}, t + 1, kb2, kc2, vb1, kb1, kc1, vb0);
+            if (t + 2 < t1) step(std::true_type{}, t + 2, kb0, kc0, vb2, kb2, kc2, vb1);
         }
     };
     run_masked(0, s1);
     for (int t = s1; t < s2; t += 3) {
         wait_older_copies();
-        step(std::false_type{}, t, kb1, vb0, kb0, vb2);
-        step(std::false_type{}, t + 1, kb2, vb1, kb1, vb0);
-        step(std::false_type{}, t + 2, kb0, vb2, kb2, vb1);
+        step(std::false_type{}, t, kb1, kc1, vb0, kb0, kc0, vb2);
+        step(std::false_type{}, t + 1, kb2, kc2, vb1, kb1, kc1, vb0);
+        step(std::false_type{}, t + 2, kb0, kc0, vb2, kb2, kc2, vb1);
     }
     run_masked(s2, n);
     // no copy may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(0xF70);
 
     const float lt = partner_sum(l_run);
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    f32x4_t ysub[NDB * 4];  // differential attention: lam * O2 / l2 of this block, in this lane's layout
+    if constexpr (DIFF) {
+        // Every wave has passed the last step's barrier and every copy has
+        // landed, so the K buffers are free.  The second map's wave of query
+        // block wv leaves lam * O2 / l2 in buffer wv (its 16-byte group r of
+        // lane l at (r * 64 + l) * 16: each access is 1 KiB contiguous), and
+        // the first map's wave of the same block, whose lanes hold the same
+        // (row, column) elements, reads it back.
+        char* xb = wv == 0 ? kb0 : wv == 1 ? kb1 : wv == 2 ? kb2 : kc0;
+        if (map == 1) {
+            const float s2 = lam_ptr[h] / lt;
+#pragma unroll
+            for (int r = 0; r < NDB * 4; ++r) {
+                const f32x4_t y = {oacc[r >> 2][4 * (r & 3) + 0] * s2, oacc[r >> 2][4 * (r & 3) + 1] * s2,
+                                   oacc[r >> 2][4 * (r & 3) + 2] * s2, oacc[r >> 2][4 * (r & 3) + 3] * s2};
+                *(f32x4_t*)(xb + (r * 64 + lane) * 16) = y;
+            }
+        }
+        lds_barrier();
+        if (map == 1) return;
+#pragma unroll
+        for (int r = 0; r < NDB * 4; ++r) ysub[r] = *(const f32x4_t*)(xb + (r * 64 + lane) * 16);
+    }
     if (!wave_live || qi >= N) return;
     if (lse_ptr != nullptr && g == 0)  // ln of the row's softmax denominator (see the 4-wave kernel)
         lse_ptr[(size_t)(b * p.Hq + h) * N + qi] = (m_run + __log2f(lt)) * 0.69314718055994531f;
-    const bool sub = lam_ptr != nullptr;  // differential attention: out -= lam * O/l
+    // second launch of the two-launch differential attention: out -= lam * O/l
+    const bool sub = !DIFF && lam_ptr != nullptr;
     const float inv = (sub ? -lam_ptr[h] : 1.f) / lt;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -1111,6 +1156,10 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             float o[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = oacc[db][4 * quad + e] * inv;
+            if constexpr (DIFF) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] -= ysub[db * 4 + quad][e];
+            }
             if (sub) {
                 const bf16x4_t prev = *dst;
 #pragma unroll
@@ -1123,16 +1172,27 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
 
 template <bool BF, int D, int MODE>
 hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
-    if constexpr (BF && (MODE == kBand || MODE == kChunk)) {
-        // (the host picks 8 waves only where the 8-wave kernel applies,
-        // including its 32-bit byte offsets into a K/V array)
-        if (p.HG * p.PB == 8) {
-            hipLaunchKernelGGL((band8_kernel<D, MODE>), dim3(p.total), dim3(kThreads8), 0, s, p);
+    if constexpr (MODE == kDiff) {
+        // one-pass differential attention: 8-wave kernel only (the host sends
+        // other shapes to two band launches)
+        if constexpr (BF) {
+            hipLaunchKernelGGL((band8_kernel<D, kDiff>), dim3(p.total), dim3(kThreads8), 0, s, p);
             return hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;
         }
+    } else {
+        if constexpr (BF && (MODE == kBand || MODE == kChunk)) {
+            // (the host picks 8 waves only where the 8-wave kernel applies,
+            // including its 32-bit byte offsets into a K/V array)
+            if (p.HG * p.PB == 8) {
+                hipLaunchKernelGGL((band8_kernel<D, MODE>), dim3(p.total), dim3(kThreads8), 0, s, p);
+                return hipGetLastError();
+            }
+        }
+        hipLaunchKernelGGL((band_fwd_kernel<BF, D, MODE>), dim3(p.total), dim3(kThreads), 0, s, p);
+        return hipGetLastError();
     }
-    hipLaunchKernelGGL((band_fwd_kernel<BF, D, MODE>), dim3(p.total), dim3(kThreads), 0, s, p);
-    return hipGetLastError();
 }
 
 template <bool BF, int D>
@@ -1140,6 +1200,7 @@ hipError_t launch_mode(int mode, const PrefillParams& p, hipStream_t s) {
     if (mode == kStrided) return launch_one<BF, D, kStrided>(p, s);
     if (mode == kChunk) return launch_one<BF, D, kChunk>(p, s);
     if (mode == kGlobal) return launch_one<BF, D, kGlobal>(p, s);
+    if (mode == kDiff) return launch_one<BF, D, kDiff>(p, s);
     return launch_one<BF, D, kBand>(p, s);
 }
 

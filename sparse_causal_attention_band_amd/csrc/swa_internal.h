@@ -9,7 +9,9 @@
 namespace swa {
 
 // ---------------------------------------------------------------- prefill
-enum { kBand = 0, kStrided = 1, kChunk = 2, kGlobal = 3 };
+// kDiff: differential attention in one pass (bf16, 8-wave kernel): two
+// query/key pairs over one V, the second map's waves beside the first's.
+enum { kBand = 0, kStrided = 1, kChunk = 2, kGlobal = 3, kDiff = 4 };
 
 struct PrefillParams {
     const void* q;
@@ -19,7 +21,9 @@ struct PrefillParams {
     const void* kring;     // chunk mode: [B, Hkv, W, d] history ring
     const void* vring;
     const int32_t* p0;     // chunk mode: [B] positions already cached
-    const float* lam;      // non-null: out -= lam[h] * result (second map of differential attention)
+    const void* q2;        // differential attention (kDiff): the second map's queries [B, Hq, N, d]
+    const void* k2;        //   and keys [B, Hkv, N, d]; q / k are the first map's
+    const float* lam;      // kDiff: out = A1 V - lam[h] A2 V; other modes, non-null: out -= lam[h] * result
     float* lse;            // non-null: [B, Hq, N] row log-sum-exp (natural log of the softmax denominator)
     const int32_t* gidx;   // global mode: sorted global positions [ng]
     int ng;
@@ -31,7 +35,8 @@ struct PrefillParams {
     int neg;      // scale < 0: queries enter with flipped sign (exact)
     int G;        // Hq / Hkv
     int HG;       // query heads of one KV head that share a workgroup
-    int PB;       // 32-query blocks per head in a workgroup (HG * PB = waves: 4 or 8)
+    int PB;       // 32-query blocks per head in a workgroup (HG * PB = waves: 4 or 8;
+                  // kDiff: 4, each block served by one wave per map)
     int nqb;      // query tiles per head
     int ngroups;  // G / HG
     int total;    // workgroups in the grid

@@ -1,7 +1,12 @@
 """GPU parity of differential sliding-window attention, (A1 - lam*A2) V,
-against the float64 oracle (fp32 and bf16, both band kernels), plus the
+against the float64 oracle: the bf16 one-pass kernel (windows under 512:
+both maps in one workgroup over one tile stream; group sizes 1 to 8, d 64
+and 128, ragged ends, W = 1 and W >= N small N, and a Mistral-shaped
+workload with W = 256 in full) and the two-launch path (fp32, and bf16 from
+W = 512 on, including the benchmark's W = 4096 workload in full); plus the
 identities the entry point must keep: lam = 0 equals the single band map
 bitwise, and identical Q/K pairs give (1 - lam) times it."""
+import math
 import sys
 
 import numpy as np
@@ -11,6 +16,8 @@ import torch
 import oracle
 import sparse_causal_attention_band_amd as swa
 from sparse_causal_attention_band_amd import inputs
+
+import full_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -46,9 +53,15 @@ def _inputs(B, Hq, Hkv, N, d, dt, seed):
 @pytest.mark.parametrize("dtype,B,Hq,Hkv,N,d,W", [
     ("f32", 1, 2, 1, 200, 64, 33),
     ("f32", 2, 4, 2, 130, 128, 64),
-    ("bf16", 1, 8, 2, 1000, 128, 256),   # 8-wave kernel
-    ("bf16", 2, 4, 4, 333, 64, 100),     # 4-wave kernel
-    ("bf16", 1, 4, 1, 77, 128, 4096),    # window beyond the sequence: the pages' causal form
+    ("bf16", 1, 8, 2, 1000, 128, 256),   # one pass: 4 heads per KV head, one query block per map
+    ("bf16", 2, 4, 4, 333, 64, 100),     # one pass: one head per KV head, 4 blocks per map
+    ("bf16", 1, 4, 1, 77, 128, 4096),    # window beyond the sequence (two launches): the pages' causal form
+    ("bf16", 1, 4, 1, 77, 128, 300),     # the same rows in one pass (W >= N)
+    ("bf16", 1, 4, 2, 700, 128, 300),    # two heads per KV head
+    ("bf16", 1, 16, 2, 400, 128, 130),   # 8 heads per KV head: two head groups
+    ("bf16", 2, 6, 2, 260, 64, 1),       # 3 heads per KV head, window 1
+    ("bf16", 1, 2, 2, 1, 64, 5),         # one token
+    ("bf16", 1, 8, 4, 2049, 64, 2049),   # full causal, ragged end
 ])
 def test_diff_vs_oracle(dtype, B, Hq, Hkv, N, d, W):
     say(f"diff {dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} W={W}")
@@ -84,3 +97,35 @@ def test_diff_identical_pairs_scale_by_one_minus_lambda():
     torch.cuda.synchronize()
     want = (1 - lam.to(DEV))[None, :, None, None] * one
     assert (out - want).abs().max().item() <= 2e-6
+
+
+@pytest.mark.parametrize("window", [4096, 256], ids=["two_launch_w4096", "one_pass_w256"])
+def test_diff_mistral_workload_full_parity(window):
+    """The benchmark's differential leg (Mistral-shaped: B=1, 32/8 heads,
+    d=128, N=16384; the second Q/K pair the position-reversed first pair,
+    lam = linspace(0.5, 0.8) over the heads) at its W = 4096 (two launches)
+    and at W = 256 (one pass): every output element against the float64
+    oracle (one head per task on the host's cores), in a NaN-filled buffer."""
+    cfg = inputs.MISTRAL
+    say(f"diff mistral-shaped workload W={window} (whole output)")
+    q, k, v = inputs.prefill_inputs(cfg)
+    q2, k2 = q.flip(2).contiguous(), k.flip(2).contiguous()
+    lam = torch.linspace(0.5, 0.8, cfg.Hq)
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
+    swa.diff_attn_fwd(*(x.to(DEV) for x in (q, k, q2, k2, v, lam)), window=window, out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    del out
+    qf, kf, q2f, k2f, vf = (x.float().numpy() for x in (q, k, q2, k2, v))
+    G, lamd = cfg.Hq // cfg.Hkv, lam.double().numpy()
+
+    def want(bh):
+        _, h = bh
+        g = slice(h // G, h // G + 1)
+        return oracle.diff_attn_fwd(qf[:, h:h + 1], kf[:, g], q2f[:, h:h + 1], k2f[:, g], vf[:, g],
+                                    lamd[h:h + 1], window, 1 / math.sqrt(cfg.d))[0, 0]
+
+    st = full_parity.compare_heads([(0, h) for h in range(cfg.Hq)], lambda bh: got[0, bh[1]], want)
+    print(f"diff mistral W={window}: {st.count} elements, max |err| {st.max_err:.3e}, mean {st.mean_err:.3e}",
+          flush=True)
+    full_parity.assert_bf16(st, f"diff mistral W={window}")
