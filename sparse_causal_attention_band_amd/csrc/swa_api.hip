@@ -113,6 +113,7 @@ int band_fwd(bool bf16, const char* name, const void* q, const void* k, const vo
     const long long total = (long long)B * Hkv * p.ngroups * p.nqb;
     if (total > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
     p.total = (int)total;
+    p.nwg = p.HG * p.PB == 8 ? swa::persistent_workgroups(p.total) : p.total;  // persistent 8-wave kernel
     hipError_t e = swa::launch_band_fwd(bf16, d, mode, p, stream);
     if (e != hipSuccess) return fail(SWA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
     return ok();
@@ -288,6 +289,7 @@ int chunk_prefill(bool bf16, const void* q, const void* k, const void* v, const 
     const long long total = (long long)B * Hkv * p.ngroups * p.nqb;
     if (total > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
     p.total = (int)total;
+    p.nwg = p.HG * p.PB == 8 ? swa::persistent_workgroups(p.total) : p.total;
     hipError_t e = swa::launch_band_fwd(bf16, d, swa::kChunk, p, stream);
     if (e != hipSuccess) return fail(SWA_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
     return ok();

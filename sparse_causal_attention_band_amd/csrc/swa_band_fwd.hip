@@ -43,6 +43,7 @@
 #include <stdint.h>
 #include <math.h>
 #include <float.h>
+#include <atomic>
 #include <type_traits>
 
 #include "swa_internal.h"
@@ -625,6 +626,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, si
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Logical block of workgroup w in its iteration `it` (-1: none left).  The
+// blocks are split into 8 contiguous ranges, one per XCD (the dispatcher
+// places workgroup w on XCD w % 8), as xcd_remap does for one block per
+// workgroup; the nwg / 8 workgroups of an XCD take its blocks in rounds of
+// nwg / 8 consecutive blocks, so the CUs of one XCD work on neighbouring
+// query blocks (shared K/V tiles in its L2), and alternate direction between
+// rounds (a snake), so the light blocks at the head of each sequence -- whose
+// bands are cut short by position 0 -- spread evenly over the workgroups.
+// nwg == total: one block per workgroup.  nwg < total: nwg is a multiple of 8.
+__device__ __forceinline__ int persistent_block(int w, int it, int nwg, int total) {
+    if (nwg >= total) return it == 0 ? xcd_remap(w, total) : -1;
+    const int xcd = w & 7, slot = w >> 3, nslot = nwg >> 3;
+    const int per = total >> 3, rem = total & 7;
+    const int base = xcd * per + min(xcd, rem), cnt = per + (xcd < rem ? 1 : 0);
+    const int idx = it * nslot + ((it & 1) ? nslot - 1 - slot : slot);
+    return idx < cnt ? base + idx : -1;
+}
+
 __device__ __forceinline__ void lds_barrier() {
     // this wave's LDS reads done, then the workgroup barrier: no fence, so
     // the copies in flight are not drained
@@ -670,504 +689,517 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     const int map = DIFF ? (wave >> 2) : 0;   // which attention map this wave computes
     const int wv = DIFF ? (wave & 3) : wave;  // the wave's query block within its map
 
-    const int L = xcd_remap(blockIdx.x, p.total);
-    const int qb = L % p.nqb;
-    int rest = L / p.nqb;
-    const int hg = rest % p.ngroups;
-    rest /= p.ngroups;
-    const int kvh = rest % p.Hkv;
-    const int b = rest / p.Hkv;
-    const int N = p.N;
-    // Chunk mode: the virtual key sequence is [placeholders | history |
-    // chunk].  The qoff = min(start, W-1) history keys come from the ring
-    // (older positions are outside every row's window); kmin < 64
-    // placeholder keys before them put the chunk's first row at the start of
-    // a 64-key tile, so that no tile mixes ring and chunk rows and every
-    // tile's copy has a single source.  Placeholders are masked like keys
-    // below the window.  Band mode: the sequence is the input (qbase = 0).
-    int qoff = 0, hslot0 = 0, kmin = 0;
-    if constexpr (CHUNK) {
-        // uniform per workgroup: scalar registers, so the copy offsets stay scalar
-        const int start = __builtin_amdgcn_readfirstlane(max(p.p0[b], 0));
-        qoff = min(start, p.W - 1);
-        hslot0 = (start - qoff) % p.W;  // ring slot of history entry 0
-        kmin = (-qoff) & (kTileN - 1);
-    }
-    const int qbase = kmin + qoff;  // virtual position of query row 0
-    const int NK = qbase + N;
-    const int W = min(p.W, NK);
-    const int BM = kQw * p.PB;
-    const int q0 = qb * BM;
-    const int h = kvh * p.G + hg * p.HG + (wv % p.HG);
-    const int qw0 = q0 + kQw * (wv / p.HG);
-    const int qi = qw0 + l32;
-    const int qv = qbase + qi;
-    const int qvw0 = qbase + qw0;
-
-    const size_t kv_head = (size_t)(b * p.Hkv + kvh) * (size_t)N * D;
-    const size_t q_head = (size_t)(b * p.Hq + h) * (size_t)N * D;
-    const elem_t* kg = (const elem_t*)p.k + kv_head;
-    const elem_t* k2g = DIFF ? (const elem_t*)p.k2 + kv_head : kg;
-    const elem_t* vg = (const elem_t*)p.v + kv_head;
-    const elem_t* qg = (const elem_t*)(map ? p.q2 : p.q) + q_head;
-    elem_t* og = (elem_t*)p.out + q_head;
-    const size_t ring_head = (size_t)(b * p.Hkv + kvh) * (size_t)p.W * D;
-    const elem_t* krg = CHUNK ? (const elem_t*)p.kring + ring_head : nullptr;
-    const elem_t* vrg = CHUNK ? (const elem_t*)p.vring + ring_head : nullptr;
-
-    const int wr = p.wr;  // right radius of a two-sided band (0: causal)
-    // every kernel argument the epilogue needs is in registers before the
-    // tile loop: a scalar load still in flight there would force every LDS
-    // wait in the loop to drain all outstanding reads
-    const float* lam_ptr = p.lam;
-    float* lse_ptr = p.lse;
-    asm volatile("" ::"s"(lam_ptr), "s"(lse_ptr));
-    const int kt_hi = min(NK - 1, qbase + q0 + BM - 1 + wr) / kTileN;
-    const int kt_lo = max(0, qbase + q0 - W + 1) / kTileN;
-    const int ntiles = kt_hi - kt_lo + 1;
-    const bool wave_live = qw0 < N;
-
-    bf16x8_t qf[NQF];
-    {
-        const uint32_t flip = p.neg ? 0x80008000u : 0u;
-        const uint32_t keep = qi < N ? 0xffffffffu : 0u;
-        const size_t qrow = (size_t)min(qi, N - 1) * D;
-#pragma unroll
-        for (int c = 0; c < NQF; ++c) {
-            u32x4_t w = *(const u32x4_t*)(qg + qrow + 16 * c + 8 * g);
-            w = (w & keep) ^ flip;
-            qf[c] = __builtin_bit_cast(bf16x8_t, w);
+    // Persistent workgroups: the grid has p.nwg <= p.total workgroups and
+    // each runs its logical blocks one after another (see persistent_block),
+    // so a CU does not wait for a new workgroup to be dispatched between
+    // blocks, and the code of the block loop stays in the instruction cache.
+    // (the one-pass differential mode keeps one block per workgroup: the
+    // block loop would push its registers past the budget)
+    for (int iter = 0;; ++iter) {
+        if (DIFF && iter > 0) break;
+        const int L = DIFF ? xcd_remap(blockIdx.x, p.total) : persistent_block(blockIdx.x, iter, p.nwg, p.total);
+        if (L < 0) break;
+        // the previous block's waves are done with every LDS buffer (and
+        // every copy has landed) before this block's prologue writes them
+        if (iter > 0) lds_barrier();
+        const int qb = L % p.nqb;
+        int rest = L / p.nqb;
+        const int hg = rest % p.ngroups;
+        rest /= p.ngroups;
+        const int kvh = rest % p.Hkv;
+        const int b = rest / p.Hkv;
+        const int N = p.N;
+        // Chunk mode: the virtual key sequence is [placeholders | history |
+        // chunk].  The qoff = min(start, W-1) history keys come from the ring
+        // (older positions are outside every row's window); kmin < 64
+        // placeholder keys before them put the chunk's first row at the start of
+        // a 64-key tile, so that no tile mixes ring and chunk rows and every
+        // tile's copy has a single source.  Placeholders are masked like keys
+        // below the window.  Band mode: the sequence is the input (qbase = 0).
+        int qoff = 0, hslot0 = 0, kmin = 0;
+        if constexpr (CHUNK) {
+            // uniform per workgroup: scalar registers, so the copy offsets stay scalar
+            const int start = __builtin_amdgcn_readfirstlane(max(p.p0[b], 0));
+            qoff = min(start, p.W - 1);
+            hslot0 = (start - qoff) % p.W;  // ring slot of history entry 0
+            kmin = (-qoff) & (kTileN - 1);
         }
-    }
+        const int qbase = kmin + qoff;  // virtual position of query row 0
+        const int NK = qbase + N;
+        const int W = min(p.W, NK);
+        const int BM = kQw * p.PB;
+        const int q0 = qb * BM;
+        const int h = kvh * p.G + hg * p.HG + (wv % p.HG);
+        const int qw0 = q0 + kQw * (wv / p.HG);
+        const int qi = qw0 + l32;
+        const int qv = qbase + qi;
+        const int qvw0 = qbase + qw0;
 
-    // V swizzle: the 64-byte quarter q of row r is stored at quarter
-    // q ^ vswz(r) (d=128: r mod 4; d=64: bit 1 of r)
-    auto vswz = [](int r) __attribute__((always_inline)) {
-        return D == 128 ? ((r & 3) << 6) : (((r >> 1) & 1) << 6);
-    };
-    const int k_lane = (((l32 >> 4) * CPR + g) << 8) + ((l32 & 15) << 4);
-    // V transpose read: row 8*g + (lane&15)/4 (+16*c2, +4), bytes
-    // 32*((lane>>4)&1) + 8*(lane&3) of quarter db (swizzled)
-    const int v_row = 8 * g + ((lane & 15) >> 2);
-    const int v_lane = v_row * RB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
-    const int vq = vswz(v_row);
+        const size_t kv_head = (size_t)(b * p.Hkv + kvh) * (size_t)N * D;
+        const size_t q_head = (size_t)(b * p.Hq + h) * (size_t)N * D;
+        const elem_t* kg = (const elem_t*)p.k + kv_head;
+        const elem_t* k2g = DIFF ? (const elem_t*)p.k2 + kv_head : kg;
+        const elem_t* vg = (const elem_t*)p.v + kv_head;
+        const elem_t* qg = (const elem_t*)(map ? p.q2 : p.q) + q_head;
+        elem_t* og = (elem_t*)p.out + q_head;
+        const size_t ring_head = (size_t)(b * p.Hkv + kvh) * (size_t)p.W * D;
+        const elem_t* krg = CHUNK ? (const elem_t*)p.kring + ring_head : nullptr;
+        const elem_t* vrg = CHUNK ? (const elem_t*)p.vring + ring_head : nullptr;
 
-    // copies: wave w fills 1 KiB blocks w, w+8, ... of the tile (lane i
-    // writes bytes 16i..16i+15 of a block).  Per block the lane's source is
-    // a fixed byte offset inside the tile's 64 rows (K: row sigma(pos),
-    // chunk ch; V: the swizzled quarter), so a tile whose rows are 64
-    // consecutive rows of one array costs one scalar base per tile (band
-    // tiles and chunk tiles, the last key row bounding the resource).  Ring
-    // tiles of chunk mode compute a slot per lane instead (the ring wraps).
-    uint32_t koff[NBLK], voff[NBLK];  // row * RB + byte in row; row = off / RB
+        const int wr = p.wr;  // right radius of a two-sided band (0: causal)
+        // every kernel argument the epilogue needs is in registers before the
+        // tile loop: a scalar load still in flight there would force every LDS
+        // wait in the loop to drain all outstanding reads
+        const float* lam_ptr = p.lam;
+        float* lse_ptr = p.lse;
+        asm volatile("" ::"s"(lam_ptr), "s"(lse_ptr));
+        const int kt_hi = min(NK - 1, qbase + q0 + BM - 1 + wr) / kTileN;
+        const int kt_lo = max(0, qbase + q0 - W + 1) / kTileN;
+        const int ntiles = kt_hi - kt_lo + 1;
+        const bool wave_live = qw0 < N;
+
+        bf16x8_t qf[NQF];
+        {
+            const uint32_t flip = p.neg ? 0x80008000u : 0u;
+            const uint32_t keep = qi < N ? 0xffffffffu : 0u;
+            const size_t qrow = (size_t)min(qi, N - 1) * D;
 #pragma unroll
-    for (int it = 0; it < NBLK; ++it) {
-        const int P = (wave + 8 * it) * 1024 + lane * 16;
-        const int within = P % (CPR * 256);
-        const int pos = (P / (CPR * 256)) * 16 + ((within >> 4) & 15);
-        koff[it] = (uint32_t)(sigma(pos) * RB + ((within >> 8) << 4));
-        const int vr = P / RB;
-        voff[it] = (uint32_t)(vr * RB + ((P % RB) ^ vswz(vr)));
-    }
-    // The copies are buffer loads straight into LDS (MUBUF "lds" form).  A
-    // resource covers one (sequence, KV head) array; the byte offset of a
-    // row is a lane offset, plus a scalar tile offset when the tile's 64 rows
-    // are consecutive rows of one array.  (The global-segment form of the
-    // same copy is a FLAT instruction that may touch LDS, which makes every
-    // later LDS or memory wait in the loop drain completely.)
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg, (size_t)N * RB);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg, (size_t)N * RB);
-    const __amdgpu_buffer_rsrc_t rkr = CHUNK ? make_rsrc(krg, (size_t)p.W * RB) : rk;
-    const __amdgpu_buffer_rsrc_t rvr = CHUNK ? make_rsrc(vrg, (size_t)p.W * RB) : rv;
-    auto issue_rows = [&](int t, char* dst, const elem_t* src, __amdgpu_buffer_rsrc_t rin,
-                          __amdgpu_buffer_rsrc_t rring, const uint32_t* off) __attribute__((always_inline)) {
-        if constexpr (!CHUNK) {
-            // Band mode: one copy instruction per block whatever the tile (a
-            // branch between a contiguous and a gathered copy leaves the
-            // compiler's copy tracking unsure at the join, and it then drains
-            // all copies before the next LDS read).  The resource starts at
-            // the tile's first row and ends at the last key row, so the lane
-            // offsets are loop invariant and rows past the end read as zero
-            // (range-checked), which the mask and P = 0 make harmless.
-            const int j0 = (kt_hi - t) * kTileN;
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)j0 * D, (size_t)(NK - j0) * RB);
-#pragma unroll
-            for (int it = 0; it < NBLK; ++it)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    r, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024), 16, (int)off[it], 0, 0,
-                    0);
-            return;
+            for (int c = 0; c < NQF; ++c) {
+                u32x4_t w = *(const u32x4_t*)(qg + qrow + 16 * c + 8 * g);
+                w = (w & keep) ^ flip;
+                qf[c] = __builtin_bit_cast(bf16x8_t, w);
+            }
         }
-        // Chunk mode: a tile is all chunk rows (one scalar base into the
-        // input, rows past the end read as zero) or all ring rows (history
-        // and placeholder keys).  Ring rows take a slot per lane, wrapping at
-        // the ring's end; placeholder rows read history entry 0, which
-        // exists whenever there are placeholders, and are masked.  Source
-        // and offsets are selected, not branched on, so every step issues
-        // the same copies and the copy waits stay partial.
-        const int j0 = (kt_hi - t) * kTileN;
-        const bool ring = j0 < qbase;
-        const int c0 = max(j0 - qbase, 0);
-        const __amdgpu_buffer_rsrc_t rc = make_rsrc(src + (size_t)c0 * D, (size_t)(N - c0) * RB);
-        const __amdgpu_buffer_rsrc_t r = ring ? rring : rc;
-        const int s0 = hslot0 + j0 - kmin;  // unwrapped slot of the tile's row 0
+
+        // V swizzle: the 64-byte quarter q of row r is stored at quarter
+        // q ^ vswz(r) (d=128: r mod 4; d=64: bit 1 of r)
+        auto vswz = [](int r) __attribute__((always_inline)) {
+            return D == 128 ? ((r & 3) << 6) : (((r >> 1) & 1) << 6);
+        };
+        const int k_lane = (((l32 >> 4) * CPR + g) << 8) + ((l32 & 15) << 4);
+        // V transpose read: row 8*g + (lane&15)/4 (+16*c2, +4), bytes
+        // 32*((lane>>4)&1) + 8*(lane&3) of quarter db (swizzled)
+        const int v_row = 8 * g + ((lane & 15) >> 2);
+        const int v_lane = v_row * RB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+        const int vq = vswz(v_row);
+
+        // copies: wave w fills 1 KiB blocks w, w+8, ... of the tile (lane i
+        // writes bytes 16i..16i+15 of a block).  Per block the lane's source is
+        // a fixed byte offset inside the tile's 64 rows (K: row sigma(pos),
+        // chunk ch; V: the swizzled quarter), so a tile whose rows are 64
+        // consecutive rows of one array costs one scalar base per tile (band
+        // tiles and chunk tiles, the last key row bounding the resource).  Ring
+        // tiles of chunk mode compute a slot per lane instead (the ring wraps).
+        uint32_t koff[NBLK], voff[NBLK];  // row * RB + byte in row; row = off / RB
 #pragma unroll
         for (int it = 0; it < NBLK; ++it) {
-            const int row = (int)(off[it] / RB);
-            const uint32_t byte = off[it] % RB;
-            const uint32_t u = (uint32_t)max(s0 + row, hslot0);  // < 2W
-            const uint32_t slot = min(u, u - (uint32_t)p.W);       // u or u - W
-            const uint32_t o = ring ? slot * RB + byte : off[it];
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024), 16, (int)o, 0, 0, 0);
+            const int P = (wave + 8 * it) * 1024 + lane * 16;
+            const int within = P % (CPR * 256);
+            const int pos = (P / (CPR * 256)) * 16 + ((within >> 4) & 15);
+            koff[it] = (uint32_t)(sigma(pos) * RB + ((within >> 8) << 4));
+            const int vr = P / RB;
+            voff[it] = (uint32_t)(vr * RB + ((P % RB) ^ vswz(vr)));
         }
-    };
-    auto issue_k = [&](int t, char* kl, char* kl2) __attribute__((always_inline)) {
-        issue_rows(t, kl, kg, rk, rkr, koff);
-        if constexpr (DIFF) issue_rows(t, kl2, k2g, rk, rk, koff);
-    };
-    auto issue_v = [&](int t, char* vl) __attribute__((always_inline)) { issue_rows(t, vl, vg, rv, rvr, voff); };
-    // Every step issues the same copies (past the end of the list the last
-    // tile again, into a buffer nobody reads any more), so one fixed wait
-    // count holds: the CPS*NBLK loads of the current step may stay in flight.
-    constexpr int CPS = DIFF ? 3 : 2;  // tiles copied per step: K (K1 and K2) and V
-    auto wait_older_copies = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0xF70 | (CPS * NBLK)); };
-
-    f32x16_t oacc[NDB];
+        // The copies are buffer loads straight into LDS (MUBUF "lds" form).  A
+        // resource covers one (sequence, KV head) array; the byte offset of a
+        // row is a lane offset, plus a scalar tile offset when the tile's 64 rows
+        // are consecutive rows of one array.  (The global-segment form of the
+        // same copy is a FLAT instruction that may touch LDS, which makes every
+        // later LDS or memory wait in the loop drain completely.)
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg, (size_t)N * RB);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg, (size_t)N * RB);
+        const __amdgpu_buffer_rsrc_t rkr = CHUNK ? make_rsrc(krg, (size_t)p.W * RB) : rk;
+        const __amdgpu_buffer_rsrc_t rvr = CHUNK ? make_rsrc(vrg, (size_t)p.W * RB) : rv;
+        auto issue_rows = [&](int t, char* dst, const elem_t* src, __amdgpu_buffer_rsrc_t rin,
+                              __amdgpu_buffer_rsrc_t rring, const uint32_t* off) __attribute__((always_inline)) {
+            if constexpr (!CHUNK) {
+                // Band mode: one copy instruction per block whatever the tile (a
+                // branch between a contiguous and a gathered copy leaves the
+                // compiler's copy tracking unsure at the join, and it then drains
+                // all copies before the next LDS read).  The resource starts at
+                // the tile's first row and ends at the last key row, so the lane
+                // offsets are loop invariant and rows past the end read as zero
+                // (range-checked), which the mask and P = 0 make harmless.
+                const int j0 = (kt_hi - t) * kTileN;
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)j0 * D, (size_t)(NK - j0) * RB);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    // m_run starts at the lowest finite value rather than -inf: a row with
-    // no allowed key yet then needs no special case (its scores are -inf,
-    // exp2(-inf + FLT_MAX) = 0), and the first finite tile maximum always
-    // grows it (alpha = exp2(-FLT_MAX - m) = 0)
-    float m_run = -FLT_MAX, l_run = 0.f;
-    const float c = p.c;
-    float alpha = 1.f;
-
-    auto scores = [&](const char* kl, f32x16_t* sc) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
-#pragma unroll
-            for (int cc = 0; cc < NQF; ++cc) {
-                const bf16x8_t a = *(const bf16x8_t*)(kl + k_lane + ((kb * 2 * CPR + 2 * cc) << 8));
-                sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], sc[kb], 0, 0, 0);
+                for (int it = 0; it < NBLK; ++it)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        r, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024), 16, (int)off[it], 0, 0,
+                        0);
+                return;
             }
-        }
-    };
-    auto mask_tile = [&](int t, f32x16_t* sc) __attribute__((always_inline)) {
-        const int j0 = (kt_hi - t) * kTileN;
-        const bool edge =
-            !(j0 + kTileN - 1 <= qvw0 + wr && j0 >= qvw0 + kQw - W && j0 + kTileN <= NK && (!CHUNK || j0 >= kmin));
-        if (edge) {
-            // key of element i in block kb is j0 + 8g + C, C = kb*32 + 16*(i/8) + i%8;
-            // with x = qv - j0 - 8g its distance is x - C, so each test is one
-            // compare of a per-tile bound against a constant (the empty asm
-            // keeps the compiler from turning them into 32 loop-invariant
-            // per-lane constants)
-            const int x = qv - j0 - 8 * g;
-            int lo = x + wr;           // dist >= -wr  <=>  C <= lo
-            int hi = x - W;            // dist < W     <=>  C > hi
-            int nk = NK - j0 - 8 * g;  // key < NK     <=>  C < nk
-            if constexpr (CHUNK) hi = max(hi, kmin - 1 - j0 - 8 * g);  // key >= kmin
-            asm volatile("" : "+v"(lo), "+v"(hi), "+v"(nk));
-            // which bounds this tile can violate (wave-uniform): most edge
-            // tiles need one compare per element, not three
-            const bool need_lo = j0 + kTileN - 1 > qvw0 + wr, need_nk = j0 + kTileN > NK;
-            const bool need_hi = j0 < qvw0 + kQw - W || (CHUNK && j0 < kmin);
-            auto apply = [&](auto keep_of) __attribute__((always_inline)) {
+            // Chunk mode: a tile is all chunk rows (one scalar base into the
+            // input, rows past the end read as zero) or all ring rows (history
+            // and placeholder keys).  Ring rows take a slot per lane, wrapping at
+            // the ring's end; placeholder rows read history entry 0, which
+            // exists whenever there are placeholders, and are masked.  Source
+            // and offsets are selected, not branched on, so every step issues
+            // the same copies and the copy waits stay partial.
+            const int j0 = (kt_hi - t) * kTileN;
+            const bool ring = j0 < qbase;
+            const int c0 = max(j0 - qbase, 0);
+            const __amdgpu_buffer_rsrc_t rc = make_rsrc(src + (size_t)c0 * D, (size_t)(N - c0) * RB);
+            const __amdgpu_buffer_rsrc_t r = ring ? rring : rc;
+            const int s0 = hslot0 + j0 - kmin;  // unwrapped slot of the tile's row 0
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int C = kb * 32 + 16 * (i >> 3) + (i & 7);
-                        sc[kb][i] = keep_of(C) ? sc[kb][i] : -INFINITY;
-                    }
-            };
-            if (!need_hi && !need_nk) {
-                apply([&](int C) { return C <= lo; });
-            } else if (!need_lo && !need_nk) {
-                apply([&](int C) { return C > hi; });
-            } else {
-                apply([&](int C) { return (C <= lo) & (C < nk) & (C > hi); });
+            for (int it = 0; it < NBLK; ++it) {
+                const int row = (int)(off[it] / RB);
+                const uint32_t byte = off[it] % RB;
+                const uint32_t u = (uint32_t)max(s0 + row, hslot0);  // < 2W
+                const uint32_t slot = min(u, u - (uint32_t)p.W);       // u or u - W
+                const uint32_t o = ring ? slot * RB + byte : off[it];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    r, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024), 16, (int)o, 0, 0, 0);
             }
-        }
-    };
-    auto tile_max = [&](const f32x16_t* sc) __attribute__((always_inline)) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
-        return partner_max(mx);
-    };
-    auto softmax_head = [&](float mx) __attribute__((always_inline)) {
-        const float m_cand = fmaxf(m_run, mx * c);
-        const bool grow = m_cand > m_run + 8.f;
-        alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_cand) : 1.f;
-        m_run = grow ? m_cand : m_run;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-        }
-    };
-    // Tile work of one step, in one straight-line block: DO_PV = this tile's
-    // probabilities, row sum and P*V (from sc, vl); DO_S = the next tile's
-    // scores (into sn, from kl).  16 keys at a time, so that every matrix
-    // instruction has vector work of the same wave beside it.
-    // K fragments of one 16-key region of the score block (the
-    // contraction chunks cc = c2 * NQF/4 ..), loaded one region ahead
-    struct KFrag {
-        bf16x8_t a[NQF / 2];
-    };
-    auto load_k = [&](const char* kl, int c2, KFrag& f) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < NQF / 2; ++i) {
-            const int kb = i & 1, cc = c2 * (NQF / 4) + (i >> 1);
-            f.a[i] = *(const bf16x8_t*)(kl + k_lane + ((kb * 2 * CPR + 2 * cc) << 8));
-        }
-    };
-    // score instructions of one 16-key region (K fragments kf)
-    auto s_region = [&](int c2, const KFrag& kf, f32x16_t* sn) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < NQF / 2; ++i) {
-            const int kb = i & 1, cc = c2 * (NQF / 4) + (i >> 1);
-            sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.a[i], qf[cc], sn[kb], 0, 0, 0);
-        }
-    };
-    auto tile_work = [&](auto do_pv, auto do_s, f32x16_t* sc, f32x16_t* sn, const char* kl, const char* vl,
-                         KFrag& kf0, KFrag& kf1, auto finish_next) __attribute__((always_inline)) {
-        constexpr bool DP = decltype(do_pv)::value, DS = decltype(do_s)::value;
-        const float m_use = m_run;
-        const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-        // one running row sum, started from the rescaled old one
-        float rs = 0.f;
-        if constexpr (DP) rs = l_run * alpha;
-        bf16x8_t pb[4];
-        auto probs = [&](int c2) __attribute__((always_inline)) {
-            u32x4_t pw;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float x0 = __builtin_amdgcn_exp2f(fmaf(sc[c2 >> 1][8 * (c2 & 1) + 2 * e], c, -m_use));
-                const float x1 = __builtin_amdgcn_exp2f(fmaf(sc[c2 >> 1][8 * (c2 & 1) + 2 * e + 1], c, -m_use));
-                const bf16x2_t pr = {(__bf16)x0, (__bf16)x1};
-                rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
-                pw[e] = __builtin_bit_cast(uint32_t, pr);
-            }
-            pb[c2] = __builtin_bit_cast(bf16x8_t, pw);
-            asm volatile("" : "+v"(rs));  // keep the dot chain beside its exponentials
         };
-        // region c2: P*V of region c2 and the scores of region c2 + 1 (the
-        // scores of region 0 were issued before the softmax head)
-        auto mfmas = [&](int c2, const KFrag& kf) __attribute__((always_inline)) {
-            u32x4_t vf[NDB];
-            if constexpr (DP) {
+        auto issue_k = [&](int t, char* kl, char* kl2) __attribute__((always_inline)) {
+            issue_rows(t, kl, kg, rk, rkr, koff);
+            if constexpr (DIFF) issue_rows(t, kl2, k2g, rk, rk, koff);
+        };
+        auto issue_v = [&](int t, char* vl) __attribute__((always_inline)) { issue_rows(t, vl, vg, rv, rvr, voff); };
+        // Every step issues the same copies (past the end of the list the last
+        // tile again, into a buffer nobody reads any more), so one fixed wait
+        // count holds: the CPS*NBLK loads of the current step may stay in flight.
+        constexpr int CPS = DIFF ? 3 : 2;  // tiles copied per step: K (K1 and K2) and V
+        auto wait_older_copies = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0xF70 | (CPS * NBLK)); };
+
+        f32x16_t oacc[NDB];
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const char* vp = vl + v_lane + ((64 * db) ^ vq) + 16 * c2 * RB;
-                    const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lds_read_tr16(vp));
-                    const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, lds_read_tr16(vp + 4 * RB));
-                    vf[db] = u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+        // m_run starts at the lowest finite value rather than -inf: a row with
+        // no allowed key yet then needs no special case (its scores are -inf,
+        // exp2(-inf + FLT_MAX) = 0), and the first finite tile maximum always
+        // grows it (alpha = exp2(-FLT_MAX - m) = 0)
+        float m_run = -FLT_MAX, l_run = 0.f;
+        const float c = p.c;
+        float alpha = 1.f;
+
+        auto scores = [&](const char* kl, f32x16_t* sc) __attribute__((always_inline)) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < NQF; ++cc) {
+                    const bf16x8_t a = *(const bf16x8_t*)(kl + k_lane + ((kb * 2 * CPR + 2 * cc) << 8));
+                    sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], sc[kb], 0, 0, 0);
                 }
             }
-            if constexpr (DS) {
-                if (c2 < 2) load_k(kl, c2 + 2, (c2 & 1) ? kf1 : kf0);
+        };
+        auto mask_tile = [&](int t, f32x16_t* sc) __attribute__((always_inline)) {
+            const int j0 = (kt_hi - t) * kTileN;
+            const bool edge =
+                !(j0 + kTileN - 1 <= qvw0 + wr && j0 >= qvw0 + kQw - W && j0 + kTileN <= NK && (!CHUNK || j0 >= kmin));
+            if (edge) {
+                // key of element i in block kb is j0 + 8g + C, C = kb*32 + 16*(i/8) + i%8;
+                // with x = qv - j0 - 8g its distance is x - C, so each test is one
+                // compare of a per-tile bound against a constant (the empty asm
+                // keeps the compiler from turning them into 32 loop-invariant
+                // per-lane constants)
+                const int x = qv - j0 - 8 * g;
+                int lo = x + wr;           // dist >= -wr  <=>  C <= lo
+                int hi = x - W;            // dist < W     <=>  C > hi
+                int nk = NK - j0 - 8 * g;  // key < NK     <=>  C < nk
+                if constexpr (CHUNK) hi = max(hi, kmin - 1 - j0 - 8 * g);  // key >= kmin
+                asm volatile("" : "+v"(lo), "+v"(hi), "+v"(nk));
+                // which bounds this tile can violate (wave-uniform): most edge
+                // tiles need one compare per element, not three
+                const bool need_lo = j0 + kTileN - 1 > qvw0 + wr, need_nk = j0 + kTileN > NK;
+                const bool need_hi = j0 < qvw0 + kQw - W || (CHUNK && j0 < kmin);
+                auto apply = [&](auto keep_of) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int C = kb * 32 + 16 * (i >> 3) + (i & 7);
+                            sc[kb][i] = keep_of(C) ? sc[kb][i] : -INFINITY;
+                        }
+                };
+                if (!need_hi && !need_nk) {
+                    apply([&](int C) { return C <= lo; });
+                } else if (!need_lo && !need_nk) {
+                    apply([&](int C) { return C > hi; });
+                } else {
+                    apply([&](int C) { return (C <= lo) & (C < nk) & (C > hi); });
+                }
             }
+        };
+        auto tile_max = [&](const f32x16_t* sc) __attribute__((always_inline)) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
+            return partner_max(mx);
+        };
+        auto softmax_head = [&](float mx) __attribute__((always_inline)) {
+            const float m_cand = fmaxf(m_run, mx * c);
+            const bool grow = m_cand > m_run + 8.f;
+            alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_cand) : 1.f;
+            m_run = grow ? m_cand : m_run;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+            }
+        };
+        // Tile work of one step, in one straight-line block: DO_PV = this tile's
+        // probabilities, row sum and P*V (from sc, vl); DO_S = the next tile's
+        // scores (into sn, from kl).  16 keys at a time, so that every matrix
+        // instruction has vector work of the same wave beside it.
+        // K fragments of one 16-key region of the score block (the
+        // contraction chunks cc = c2 * NQF/4 ..), loaded one region ahead
+        struct KFrag {
+            bf16x8_t a[NQF / 2];
+        };
+        auto load_k = [&](const char* kl, int c2, KFrag& f) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < NQF / 2; ++i) {
-                if constexpr (DS) {
-                    if (c2 < 3) {
-                        const int kb = i & 1, cc = (c2 + 1) * (NQF / 4) + (i >> 1);
-                        sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.a[i], qf[cc], sn[kb], 0, 0, 0);
-                    }
-                }
-                if constexpr (DP) {
-                    const int db = i;
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[db]), pb[c2],
-                                                                      oacc[db], 0, 0, 0);
-                }
+                const int kb = i & 1, cc = c2 * (NQF / 4) + (i >> 1);
+                f.a[i] = *(const bf16x8_t*)(kl + k_lane + ((kb * 2 * CPR + 2 * cc) << 8));
             }
         };
-        if constexpr (DP) probs(0);
-        float mx_next = 0.f;
+        // score instructions of one 16-key region (K fragments kf)
+        auto s_region = [&](int c2, const KFrag& kf, f32x16_t* sn) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c2 = 0; c2 < 4; ++c2) {
+            for (int i = 0; i < NQF / 2; ++i) {
+                const int kb = i & 1, cc = c2 * (NQF / 4) + (i >> 1);
+                sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.a[i], qf[cc], sn[kb], 0, 0, 0);
+            }
+        };
+        auto tile_work = [&](auto do_pv, auto do_s, f32x16_t* sc, f32x16_t* sn, const char* kl, const char* vl,
+                             KFrag& kf0, KFrag& kf1, auto finish_next) __attribute__((always_inline)) {
+            constexpr bool DP = decltype(do_pv)::value, DS = decltype(do_s)::value;
+            const float m_use = m_run;
+            const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+            // one running row sum, started from the rescaled old one
+            float rs = 0.f;
+            if constexpr (DP) rs = l_run * alpha;
+            bf16x8_t pb[4];
+            auto probs = [&](int c2) __attribute__((always_inline)) {
+                u32x4_t pw;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x0 = __builtin_amdgcn_exp2f(fmaf(sc[c2 >> 1][8 * (c2 & 1) + 2 * e], c, -m_use));
+                    const float x1 = __builtin_amdgcn_exp2f(fmaf(sc[c2 >> 1][8 * (c2 & 1) + 2 * e + 1], c, -m_use));
+                    const bf16x2_t pr = {(__bf16)x0, (__bf16)x1};
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+                    pw[e] = __builtin_bit_cast(uint32_t, pr);
+                }
+                pb[c2] = __builtin_bit_cast(bf16x8_t, pw);
+                asm volatile("" : "+v"(rs));  // keep the dot chain beside its exponentials
+            };
+            // region c2: P*V of region c2 and the scores of region c2 + 1 (the
+            // scores of region 0 were issued before the softmax head)
+            auto mfmas = [&](int c2, const KFrag& kf) __attribute__((always_inline)) {
+                u32x4_t vf[NDB];
+                if constexpr (DP) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const char* vp = vl + v_lane + ((64 * db) ^ vq) + 16 * c2 * RB;
+                        const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lds_read_tr16(vp));
+                        const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, lds_read_tr16(vp + 4 * RB));
+                        vf[db] = u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
+                    }
+                }
+                if constexpr (DS) {
+                    if (c2 < 2) load_k(kl, c2 + 2, (c2 & 1) ? kf1 : kf0);
+                }
+#pragma unroll
+                for (int i = 0; i < NQF / 2; ++i) {
+                    if constexpr (DS) {
+                        if (c2 < 3) {
+                            const int kb = i & 1, cc = (c2 + 1) * (NQF / 4) + (i >> 1);
+                            sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.a[i], qf[cc], sn[kb], 0, 0, 0);
+                        }
+                    }
+                    if constexpr (DP) {
+                        const int db = i;
+                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[db]), pb[c2],
+                                                                          oacc[db], 0, 0, 0);
+                    }
+                }
+            };
+            if constexpr (DP) probs(0);
+            float mx_next = 0.f;
+#pragma unroll
+            for (int c2 = 0; c2 < 4; ++c2) {
+                __builtin_amdgcn_sched_barrier(0);
+                // the last region masks the next block (edge tiles) and takes its
+                // row maximum beside this tile's last P*V instructions
+                if (c2 == 3) mx_next = finish_next();
+                mfmas(c2, (c2 & 1) ? kf0 : kf1);
+                if constexpr (DP) {
+                    if (c2 < 3) probs(c2 + 1);
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
-            // the last region masks the next block (edge tiles) and takes its
-            // row maximum beside this tile's last P*V instructions
-            if (c2 == 3) mx_next = finish_next();
-            mfmas(c2, (c2 & 1) ? kf0 : kf1);
-            if constexpr (DP) {
-                if (c2 < 3) probs(c2 + 1);
-            }
+            if constexpr (DP) l_run = rs;
+            return mx_next;
+        };
+
+        const int n = ntiles;
+        {
+            // V(0), the top tile, may end past the last key row; whether or not
+            // a range-checked copy writes its zeros, those rows of vb0 must hold
+            // finite values (they meet P = 0), so the buffer starts zeroed (the
+            // barrier below orders these writes before the copies)
+            const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int it = 0; it < TILE_BYTES / (kThreads8 * 16); ++it) *(u32x4_t*)(vb0 + (it * kThreads8 + tid) * 16) = z;
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (DP) l_run = rs;
-        return mx_next;
-    };
-
-    const int n = ntiles;
-    {
-        // V(0), the top tile, may end past the last key row; whether or not
-        // a range-checked copy writes its zeros, those rows of vb0 must hold
-        // finite values (they meet P = 0), so the buffer starts zeroed (the
-        // barrier below orders these writes before the copies)
-        const u32x4_t z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int it = 0; it < TILE_BYTES / (kThreads8 * 16); ++it) *(u32x4_t*)(vb0 + (it * kThreads8 + tid) * 16) = z;
-    }
-    // prologue: K(0), scores of tile 0; then K(1), V(0), K(2), V(1) in flight
-    issue_k(0, kb0, kc0);
-    __builtin_amdgcn_s_waitcnt(0xF70);
-    lds_barrier();
-    f32x16_t scur[2];
-    scores(map ? kc0 : kb0, scur);
-    mask_tile(0, scur);
-    float mx_cur = tile_max(scur);
-    lds_barrier();  // tile 0's K reads are done before K(3) lands in kb0
-    issue_k(min(1, n - 1), kb1, kc1);
-    issue_v(0, vb0);
-    issue_k(min(2, n - 1), kb2, kc2);
-    issue_v(min(1, n - 1), vb1);
-    wait_older_copies();
-    lds_barrier();
-
-    // step t: scores of t+1 from kn, P*V of t from vc; K(t+3) -> ki, V(t+2) -> vi.
-    // MASKED: tile t+1 may be an edge tile of this wave (the wave-uniform
-    // test in mask_tile decides); otherwise it is known to be interior for
-    // every wave and the step has no mask code at all.
-    // kn2, ki2: the second map's K buffers (differential attention)
-    auto step = [&](auto masked, int t, const char* kn1, const char* kn2, const char* vc, char* ki, char* ki2,
-                    char* vi) __attribute__((always_inline)) {
-        constexpr bool MASKED = decltype(masked)::value;
-        issue_k(min(t + 3, n - 1), ki, ki2);
-        issue_v(min(t + 2, n - 1), vi);
-        const char* kn = map ? kn2 : kn1;  // this wave's K buffer
-        // K fragments of the next tile's first two regions; its first
-        // region's scores, then this tile's head (row maximum taken in the
-        // previous step)
-        KFrag kf0, kf1;
-        load_k(kn, 0, kf0);
-        load_k(kn, 1, kf1);
-        f32x16_t snext[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) snext[kb][i] = 0.f;
-        // past the last tile the score block reads stale data and is discarded
-        s_region(0, kf0, snext);
-        softmax_head(mx_cur);
-        mx_cur = tile_work(std::true_type{}, std::true_type{}, scur, snext, kn, vc, kf0, kf1,
-                           [&]() __attribute__((always_inline)) {
-                               if constexpr (MASKED) {
-                                   if (t + 1 < n) mask_tile(t + 1, snext);
-                               }
-                               return tile_max(snext);
-                           });
-        scur[0] = snext[0];
-        scur[1] = snext[1];
+        // prologue: K(0), scores of tile 0; then K(1), V(0), K(2), V(1) in flight
+        issue_k(0, kb0, kc0);
+        __builtin_amdgcn_s_waitcnt(0xF70);
+        lds_barrier();
+        f32x16_t scur[2];
+        scores(map ? kc0 : kb0, scur);
+        mask_tile(0, scur);
+        float mx_cur = tile_max(scur);
+        lds_barrier();  // tile 0's K reads are done before K(3) lands in kb0
+        issue_k(min(1, n - 1), kb1, kc1);
+        issue_v(0, vb0);
+        issue_k(min(2, n - 1), kb2, kc2);
+        issue_v(min(1, n - 1), vb1);
         wait_older_copies();
         lds_barrier();
-    };
-    // Tiles t_a .. t_b lie inside the band of every row of the workgroup
-    // (interior for every wave: after the diagonal tiles of its lowest rows,
-    // at or above the window start of its highest rows, whole, and in chunk
-    // mode past the placeholder keys).  Step t masks tile t+1, so steps
-    // [s1, s2), with t_a <= t+1 <= t_b, need no mask.  The steps run in three
-    // segments -- masked, mask-free, masked -- each starting at a multiple
-    // of three, so every segment rotates the static buffers the same way;
-    // the mask-free segment is a whole number of three-step rounds, so its
-    // loop body has no branch at all (at W = 4096 it holds all but ~4 of the
-    // ~66 steps).
-    const int lo_key = qbase + q0 + wr;                // last key of the lowest rows' band
-    const int hi_key = qbase + q0 + kQw * p.PB - W;    // first key of the highest rows' band
-    int t_a = max(max(kt_hi - ((lo_key - (kTileN - 1)) >> 6), kt_hi - ((NK - kTileN) >> 6)), 0);
-    int t_b = min(kt_hi - ((hi_key + kTileN - 1) >> 6), n - 1);
-    if constexpr (CHUNK) t_b = min(t_b, kt_hi - ((kmin + kTileN - 1) >> 6));
-    int s1 = n, s2 = n;
-    if (t_a <= t_b) {
-        s1 = min((max(t_a - 1, 0) + 2) / 3 * 3, n);
-        s2 = s1 + max(0, t_b - s1) / 3 * 3;  // <= t_b < n; the last step's t+1 = s2 <= t_b
-    }
-    auto run_masked = [&](int t0, int t1) __attribute__((always_inline)) {
-        for (int t = t0; t < t1; t += 3) {
-            // (already true here; stated so that the compiler's own copy
-            // tracking does not lose it at the loop head)
+
+        // step t: scores of t+1 from kn, P*V of t from vc; K(t+3) -> ki, V(t+2) -> vi.
+        // MASKED: tile t+1 may be an edge tile of this wave (the wave-uniform
+        // test in mask_tile decides); otherwise it is known to be interior for
+        // every wave and the step has no mask code at all.
+        // kn2, ki2: the second map's K buffers (differential attention)
+        auto step = [&](auto masked, int t, const char* kn1, const char* kn2, const char* vc, char* ki, char* ki2,
+                        char* vi) __attribute__((always_inline)) {
+            constexpr bool MASKED = decltype(masked)::value;
+            issue_k(min(t + 3, n - 1), ki, ki2);
+            issue_v(min(t + 2, n - 1), vi);
+            const char* kn = map ? kn2 : kn1;  // this wave's K buffer
+            // K fragments of the next tile's first two regions; its first
+            // region's scores, then this tile's head (row maximum taken in the
+            // previous step)
+            KFrag kf0, kf1;
+            load_k(kn, 0, kf0);
+            load_k(kn, 1, kf1);
+            f32x16_t snext[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) snext[kb][i] = 0.f;
+            // past the last tile the score block reads stale data and is discarded
+            s_region(0, kf0, snext);
+            softmax_head(mx_cur);
+            mx_cur = tile_work(std::true_type{}, std::true_type{}, scur, snext, kn, vc, kf0, kf1,
+                               [&]() __attribute__((always_inline)) {
+                                   if constexpr (MASKED) {
+                                       if (t + 1 < n) mask_tile(t + 1, snext);
+                                   }
+                                   return tile_max(snext);
+                               });
+            scur[0] = snext[0];
+            scur[1] = snext[1];
             wait_older_copies();
-            step(std::true_type{}, t, kb1, kc1, vb0, kb0, kc0, vb2);
-            if (t + 1 < t1) step(std::true_type{}, t + 1, kb2, kc2, vb1, kb1, kc1, vb0);
-            if (t + 2 < t1) step(std::true_type{}, t + 2, kb0, kc0, vb2, kb2, kc2, vb1);
+            lds_barrier();
+        };
+        // Tiles t_a .. t_b lie inside the band of every row of the workgroup
+        // (interior for every wave: after the diagonal tiles of its lowest rows,
+        // at or above the window start of its highest rows, whole, and in chunk
+        // mode past the placeholder keys).  Step t masks tile t+1, so steps
+        // [s1, s2), with t_a <= t+1 <= t_b, need no mask.  The steps run in three
+        // segments -- masked, mask-free, masked -- each starting at a multiple
+        // of three, so every segment rotates the static buffers the same way;
+        // the mask-free segment is a whole number of three-step rounds, so its
+        // loop body has no branch at all (at W = 4096 it holds all but ~4 of the
+        // ~66 steps).
+        const int lo_key = qbase + q0 + wr;                // last key of the lowest rows' band
+        const int hi_key = qbase + q0 + kQw * p.PB - W;    // first key of the highest rows' band
+        int t_a = max(max(kt_hi - ((lo_key - (kTileN - 1)) >> 6), kt_hi - ((NK - kTileN) >> 6)), 0);
+        int t_b = min(kt_hi - ((hi_key + kTileN - 1) >> 6), n - 1);
+        if constexpr (CHUNK) t_b = min(t_b, kt_hi - ((kmin + kTileN - 1) >> 6));
+        int s1 = n, s2 = n;
+        if (t_a <= t_b) {
+            s1 = min((max(t_a - 1, 0) + 2) / 3 * 3, n);
+            s2 = s1 + max(0, t_b - s1) / 3 * 3;  // <= t_b < n; the last step's t+1 = s2 <= t_b
         }
-    };
-    run_masked(0, s1);
-    for (int t = s1; t < s2; t += 3) {
-        wait_older_copies();
-        step(std::false_type{}, t, kb1, kc1, vb0, kb0, kc0, vb2);
-        step(std::false_type{}, t + 1, kb2, kc2, vb1, kb1, kc1, vb0);
-        step(std::false_type{}, t + 2, kb0, kc0, vb2, kb2, kc2, vb1);
-    }
-    run_masked(s2, n);
-    // no copy may still be writing this workgroup's LDS when it ends
-    __builtin_amdgcn_s_waitcnt(0xF70);
+        auto run_masked = [&](int t0, int t1) __attribute__((always_inline)) {
+            for (int t = t0; t < t1; t += 3) {
+                // (already true here; stated so that the compiler's own copy
+                // tracking does not lose it at the loop head)
+                wait_older_copies();
+                step(std::true_type{}, t, kb1, kc1, vb0, kb0, kc0, vb2);
+                if (t + 1 < t1) step(std::true_type{}, t + 1, kb2, kc2, vb1, kb1, kc1, vb0);
+                if (t + 2 < t1) step(std::true_type{}, t + 2, kb0, kc0, vb2, kb2, kc2, vb1);
+            }
+        };
+        run_masked(0, s1);
+        for (int t = s1; t < s2; t += 3) {
+            wait_older_copies();
+            step(std::false_type{}, t, kb1, kc1, vb0, kb0, kc0, vb2);
+            step(std::false_type{}, t + 1, kb2, kc2, vb1, kb1, kc1, vb0);
+            step(std::false_type{}, t + 2, kb0, kc0, vb2, kb2, kc2, vb1);
+        }
+        run_masked(s2, n);
+        // no copy may still be writing this workgroup's LDS when it ends
+        __builtin_amdgcn_s_waitcnt(0xF70);
 
-    const float lt = partner_sum(l_run);
-    typedef float f32x4_t __attribute__((ext_vector_type(4)));
-    f32x4_t ysub[NDB * 4];  // differential attention: lam * O2 / l2 of this block, in this lane's layout
-    if constexpr (DIFF) {
-        // Every wave has passed the last step's barrier and every copy has
-        // landed, so the K buffers are free.  The second map's wave of query
-        // block wv leaves lam * O2 / l2 in buffer wv (its 16-byte group r of
-        // lane l at (r * 64 + l) * 16: each access is 1 KiB contiguous), and
-        // the first map's wave of the same block, whose lanes hold the same
-        // (row, column) elements, reads it back.
-        char* xb = wv == 0 ? kb0 : wv == 1 ? kb1 : wv == 2 ? kb2 : kc0;
-        if (map == 1) {
-            const float s2 = lam_ptr[h] / lt;
+        const float lt = partner_sum(l_run);
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        f32x4_t ysub[NDB * 4];  // differential attention: lam * O2 / l2 of this block, in this lane's layout
+        if constexpr (DIFF) {
+            // Every wave has passed the last step's barrier and every copy has
+            // landed, so the K buffers are free.  The second map's wave of query
+            // block wv leaves lam * O2 / l2 in buffer wv (its 16-byte group r of
+            // lane l at (r * 64 + l) * 16: each access is 1 KiB contiguous), and
+            // the first map's wave of the same block, whose lanes hold the same
+            // (row, column) elements, reads it back.
+            char* xb = wv == 0 ? kb0 : wv == 1 ? kb1 : wv == 2 ? kb2 : kc0;
+            if (map == 1) {
+                const float s2 = lam_ptr[h] / lt;
 #pragma unroll
-            for (int r = 0; r < NDB * 4; ++r) {
-                const f32x4_t y = {oacc[r >> 2][4 * (r & 3) + 0] * s2, oacc[r >> 2][4 * (r & 3) + 1] * s2,
-                                   oacc[r >> 2][4 * (r & 3) + 2] * s2, oacc[r >> 2][4 * (r & 3) + 3] * s2};
-                *(f32x4_t*)(xb + (r * 64 + lane) * 16) = y;
+                for (int r = 0; r < NDB * 4; ++r) {
+                    const f32x4_t y = {oacc[r >> 2][4 * (r & 3) + 0] * s2, oacc[r >> 2][4 * (r & 3) + 1] * s2,
+                                       oacc[r >> 2][4 * (r & 3) + 2] * s2, oacc[r >> 2][4 * (r & 3) + 3] * s2};
+                    *(f32x4_t*)(xb + (r * 64 + lane) * 16) = y;
+                }
             }
-        }
-        lds_barrier();
-        if (map == 1) return;
+            lds_barrier();
+            if (map == 1) continue;
 #pragma unroll
-        for (int r = 0; r < NDB * 4; ++r) ysub[r] = *(const f32x4_t*)(xb + (r * 64 + lane) * 16);
+            for (int r = 0; r < NDB * 4; ++r) ysub[r] = *(const f32x4_t*)(xb + (r * 64 + lane) * 16);
+        }
+        if (!wave_live || qi >= N) continue;
+        if (lse_ptr != nullptr && g == 0)  // ln of the row's softmax denominator (see the 4-wave kernel)
+            lse_ptr[(size_t)(b * p.Hq + h) * N + qi] = (m_run + __log2f(lt)) * 0.69314718055994531f;
+        // second launch of the two-launch differential attention: out -= lam * O/l
+        const bool sub = !DIFF && lam_ptr != nullptr;
+        const float inv = (sub ? -lam_ptr[h] : 1.f) / lt;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int quad = 0; quad < 4; ++quad) {
+                const int d0 = db * 32 + 8 * quad + 4 * g;
+                typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                bf16x4_t* dst = (bf16x4_t*)(og + (size_t)qi * D + d0);
+                float o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = oacc[db][4 * quad + e] * inv;
+                if constexpr (DIFF) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] -= ysub[db * 4 + quad][e];
+                }
+                if (sub) {
+                    const bf16x4_t prev = *dst;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] += (float)prev[e];
+                }
+                const bf16x4_t ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+                *dst = ob;
+            }
     }
-    if (!wave_live || qi >= N) return;
-    if (lse_ptr != nullptr && g == 0)  // ln of the row's softmax denominator (see the 4-wave kernel)
-        lse_ptr[(size_t)(b * p.Hq + h) * N + qi] = (m_run + __log2f(lt)) * 0.69314718055994531f;
-    // second launch of the two-launch differential attention: out -= lam * O/l
-    const bool sub = !DIFF && lam_ptr != nullptr;
-    const float inv = (sub ? -lam_ptr[h] : 1.f) / lt;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int quad = 0; quad < 4; ++quad) {
-            const int d0 = db * 32 + 8 * quad + 4 * g;
-            typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-            bf16x4_t* dst = (bf16x4_t*)(og + (size_t)qi * D + d0);
-            float o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = oacc[db][4 * quad + e] * inv;
-            if constexpr (DIFF) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] -= ysub[db * 4 + quad][e];
-            }
-            if (sub) {
-                const bf16x4_t prev = *dst;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] += (float)prev[e];
-            }
-            const bf16x4_t ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-            *dst = ob;
-        }
 }
 
 template <bool BF, int D, int MODE>
@@ -1176,7 +1208,7 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
         // one-pass differential attention: 8-wave kernel only (the host sends
         // other shapes to two band launches)
         if constexpr (BF) {
-            hipLaunchKernelGGL((band8_kernel<D, kDiff>), dim3(p.total), dim3(kThreads8), 0, s, p);
+            hipLaunchKernelGGL((band8_kernel<D, kDiff>), dim3(p.nwg), dim3(kThreads8), 0, s, p);
             return hipGetLastError();
         } else {
             return hipErrorInvalidValue;
@@ -1186,7 +1218,7 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
             // (the host picks 8 waves only where the 8-wave kernel applies,
             // including its 32-bit byte offsets into a K/V array)
             if (p.HG * p.PB == 8) {
-                hipLaunchKernelGGL((band8_kernel<D, MODE>), dim3(p.total), dim3(kThreads8), 0, s, p);
+                hipLaunchKernelGGL((band8_kernel<D, MODE>), dim3(p.nwg), dim3(kThreads8), 0, s, p);
                 return hipGetLastError();
             }
         }
@@ -1205,6 +1237,21 @@ hipError_t launch_mode(int mode, const PrefillParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+int persistent_workgroups(int total) {
+    // CUs of the current device, looked up once per device (a racing first
+    // lookup on two threads stores the same value)
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return total;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) return total;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    n &= ~7;
+    return total > n ? n : total;
+}
 
 hipError_t launch_band_fwd(bool bf16, int d, int mode, const PrefillParams& p, hipStream_t s) {
     if (bf16) return d == 128 ? launch_mode<true, 128>(mode, p, s) : launch_mode<true, 64>(mode, p, s);

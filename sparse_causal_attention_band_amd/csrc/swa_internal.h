@@ -39,8 +39,13 @@ struct PrefillParams {
                   // kDiff: 4, each block served by one wave per map)
     int nqb;      // query tiles per head
     int ngroups;  // G / HG
-    int total;    // workgroups in the grid
+    int total;    // logical blocks (query tiles x head groups x KV heads x sequences)
+    int nwg;      // workgroups in the grid: total, or (8-wave kernel) fewer persistent ones
 };
+
+// Persistent workgroups of the 8-wave kernel: one per CU (its LDS and
+// registers allow one), a multiple of 8, at most `total`.
+int persistent_workgroups(int total);
 
 // Launch the band kernel for one (dtype, head dim, mode) combination.
 hipError_t launch_band_fwd(bool bf16, int d, int mode, const PrefillParams& p, hipStream_t s);
