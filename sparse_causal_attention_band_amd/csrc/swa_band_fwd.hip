@@ -681,6 +681,17 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     __shared__ __attribute__((aligned(16))) char kc0[DIFF ? TILE_BYTES : 16];
     __shared__ __attribute__((aligned(16))) char kc1[DIFF ? TILE_BYTES : 16];
     __shared__ __attribute__((aligned(16))) char kc2[DIFF ? TILE_BYTES : 16];
+    // Band mode streams from one block into the next (see `pre` below): each
+    // wave stages its 32 query rows of the next block in its region of these
+    // (two waves per array), 16-byte chunk k of row r at (k * 32 + r) * 16.
+    // Four arrays the size of a tile buffer, declared last, are placed after
+    // the tile buffers, whose LDS reads then keep small address offsets.
+    constexpr bool STREAM = MODE == kBand;
+    constexpr int QST = STREAM ? 2 * kQw * RB : 16;
+    __shared__ __attribute__((aligned(16))) char qs0[QST];
+    __shared__ __attribute__((aligned(16))) char qs1[QST];
+    __shared__ __attribute__((aligned(16))) char qs2[QST];
+    __shared__ __attribute__((aligned(16))) char qs3[QST];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -699,9 +710,15 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         if (DIFF && iter > 0) break;
         const int L = DIFF ? xcd_remap(blockIdx.x, p.total) : persistent_block(blockIdx.x, iter, p.nwg, p.total);
         if (L < 0) break;
-        // the previous block's waves are done with every LDS buffer (and
-        // every copy has landed) before this block's prologue writes them
-        if (iter > 0) lds_barrier();
+        // Band mode: the previous block's last steps already copied this
+        // block's first K and V tiles into the buffers its prologue would fill
+        // and staged its queries (its tile list is padded to a multiple of
+        // three steps, so the buffer rotation continues unchanged), so the
+        // prologue only computes the first tile's scores.  Other modes: the
+        // previous block's waves are done with every LDS buffer (and every
+        // copy has landed) before this block's prologue writes them.
+        const bool pre = STREAM && iter > 0;
+        if (iter > 0 && !pre) lds_barrier();
         const int qb = L % p.nqb;
         int rest = L / p.nqb;
         const int hg = rest % p.ngroups;
@@ -757,17 +774,58 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         const int kt_lo = max(0, qbase + q0 - W + 1) / kTileN;
         const int ntiles = kt_hi - kt_lo + 1;
         const bool wave_live = qw0 < N;
+        // band mode: this workgroup's next block, whose first tiles and queries
+        // are copied during this block's last steps (uniform scalars)
+        const int Ln = STREAM ? persistent_block(blockIdx.x, iter + 1, p.nwg, p.total) : -1;
+        const bool has_next = Ln >= 0;
+        // its first tile, tile count, arrays and this wave's rows: set just
+        // before the last masked segment, the only code that reads them (so
+        // they take no registers in the loops before it)
+        int kt_hi_n, n_n, qw0_n;
+        const elem_t* kg_n;
+        const elem_t* vg_n;
+        const elem_t* qg_n;
+        auto next_block = [&]() __attribute__((always_inline)) {
+            const int Lx = max(Ln, 0);
+            const int qb_n = Lx % p.nqb;
+            int r_n = Lx / p.nqb;
+            const int hg_n = r_n % p.ngroups;
+            r_n /= p.ngroups;
+            const int kvh_n = r_n % p.Hkv, b_n = r_n / p.Hkv;
+            const int q0_n = qb_n * BM;
+            kt_hi_n = min(NK - 1, q0_n + BM - 1 + wr) / kTileN;
+            n_n = kt_hi_n - max(0, q0_n - W + 1) / kTileN + 1;
+            const size_t kv_n = (size_t)(b_n * p.Hkv + kvh_n) * (size_t)N * D;
+            kg_n = (const elem_t*)p.k + kv_n;
+            vg_n = (const elem_t*)p.v + kv_n;
+            qg_n = (const elem_t*)p.q + (size_t)(b_n * p.Hq + kvh_n * p.G + hg_n * p.HG + (wv % p.HG)) * (size_t)N * D;
+            qw0_n = q0_n + kQw * (wv / p.HG);
+        };
+        // steps of this block: its tiles, then (with a next block) placeholder
+        // steps that only copy, up to a multiple of three
+        const int n3 = has_next ? (ntiles + 2) / 3 * 3 : ntiles;
 
         bf16x8_t qf[NQF];
         {
             const uint32_t flip = p.neg ? 0x80008000u : 0u;
             const uint32_t keep = qi < N ? 0xffffffffu : 0u;
             const size_t qrow = (size_t)min(qi, N - 1) * D;
+            if (pre) {
+                // staged by the previous block: chunk 2c + g of row l32
+                const char* qs = (wave < 4 ? (wave < 2 ? qs0 : qs1) : (wave < 6 ? qs2 : qs3)) + (wave & 1) * (kQw * RB);
 #pragma unroll
-            for (int c = 0; c < NQF; ++c) {
-                u32x4_t w = *(const u32x4_t*)(qg + qrow + 16 * c + 8 * g);
-                w = (w & keep) ^ flip;
-                qf[c] = __builtin_bit_cast(bf16x8_t, w);
+                for (int c = 0; c < NQF; ++c) {
+                    u32x4_t w = *(const u32x4_t*)(qs + (((2 * c + g) * kQw + l32) << 4));
+                    w = (w & keep) ^ flip;
+                    qf[c] = __builtin_bit_cast(bf16x8_t, w);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NQF; ++c) {
+                    u32x4_t w = *(const u32x4_t*)(qg + qrow + 16 * c + 8 * g);
+                    w = (w & keep) ^ flip;
+                    qf[c] = __builtin_bit_cast(bf16x8_t, w);
+                }
             }
         }
 
@@ -853,11 +911,57 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
                     r, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024), 16, (int)o, 0, 0, 0);
             }
         };
-        auto issue_k = [&](int t, char* kl, char* kl2) __attribute__((always_inline)) {
-            issue_rows(t, kl, kg, rk, rkr, koff);
-            if constexpr (DIFF) issue_rows(t, kl2, k2g, rk, rk, koff);
+        // band mode: tile kt (absolute) of the K or V array `src`, as in issue_rows
+        auto issue_band = [&](int kt, char* dst, const elem_t* src, const uint32_t* off) __attribute__((always_inline)) {
+            const int j0 = kt * kTileN;
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)j0 * D, (size_t)(NK - j0) * RB);
+#pragma unroll
+            for (int it = 0; it < NBLK; ++it)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    r, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024), 16, (int)off[it], 0, 0, 0);
         };
-        auto issue_v = [&](int t, char* vl) __attribute__((always_inline)) { issue_rows(t, vl, vg, rv, rvr, voff); };
+        // copy stream position sp: the block's tile min(sp, n-1) (past the end
+        // of its list the last tile again, into a buffer nobody reads), or in
+        // band mode, from position n3 on, the next block's first tiles.  Only
+        // the last masked segment and the copy-only steps reach position n3
+        // (CROSS); there source and tile are selected, not branched on, so
+        // every step issues the same copies.
+        auto issue_k = [&](auto cross, int sp, char* kl, char* kl2) __attribute__((always_inline)) {
+            if constexpr (STREAM && decltype(cross)::value) {
+                const bool nx = has_next && sp >= n3;
+                issue_band(nx ? kt_hi_n - min(sp - n3, n_n - 1) : kt_hi - min(sp, ntiles - 1), kl, nx ? kg_n : kg, koff);
+            } else if constexpr (STREAM) {
+                issue_band(kt_hi - min(sp, ntiles - 1), kl, kg, koff);
+            } else {
+                issue_rows(min(sp, ntiles - 1), kl, kg, rk, rkr, koff);
+                if constexpr (DIFF) issue_rows(min(sp, ntiles - 1), kl2, k2g, rk, rk, koff);
+            }
+        };
+        auto issue_v = [&](auto cross, int sp, char* vl) __attribute__((always_inline)) {
+            if constexpr (STREAM && decltype(cross)::value) {
+                const bool nx = has_next && sp >= n3;
+                issue_band(nx ? kt_hi_n - min(sp - n3, n_n - 1) : kt_hi - min(sp, ntiles - 1), vl, nx ? vg_n : vg, voff);
+            } else if constexpr (STREAM) {
+                issue_band(kt_hi - min(sp, ntiles - 1), vl, vg, voff);
+            } else {
+                issue_rows(min(sp, ntiles - 1), vl, vg, rv, rvr, voff);
+            }
+        };
+        // band mode: this wave's 32 query rows of the next block into its qst
+        // region (lane i of 1 KiB block b fetches chunk 2b + i/32 of row i%32;
+        // the range check zeroes rows past the sequence)
+        auto stage_q = [&]() __attribute__((always_inline)) {
+            if constexpr (STREAM) {
+                const __amdgpu_buffer_rsrc_t r =
+                    make_rsrc(qg_n + (size_t)min(qw0_n, N) * D, (size_t)max(N - qw0_n, 0) * RB);
+                char* qs = (wave < 4 ? (wave < 2 ? qs0 : qs1) : (wave < 6 ? qs2 : qs3)) + (wave & 1) * (kQw * RB);
+#pragma unroll
+                for (int b4 = 0; b4 < RB / 32; ++b4)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        r, (__attribute__((address_space(3))) void*)(qs + b4 * 1024), 16,
+                        l32 * RB + ((2 * b4 + g) << 4), 0, 0, 0);
+            }
+        };
         // Every step issues the same copies (past the end of the list the last
         // tile again, into a buffer nobody reads any more), so one fixed wait
         // count holds: the CPS*NBLK loads of the current step may stay in flight.
@@ -1043,41 +1147,49 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         };
 
         const int n = ntiles;
-        {
-            // V(0), the top tile, may end past the last key row; whether or not
-            // a range-checked copy writes its zeros, those rows of vb0 must hold
-            // finite values (they meet P = 0), so the buffer starts zeroed (the
-            // barrier below orders these writes before the copies)
-            const u32x4_t z = {0u, 0u, 0u, 0u};
+        if (!pre) {
+            {
+                // V(0), the top tile, may end past the last key row; whether or
+                // not a range-checked copy writes its zeros, those rows of vb0
+                // must hold finite values (they meet P = 0), so the buffer starts
+                // zeroed (the barrier below orders these writes before the
+                // copies; later blocks find finite tile data there)
+                const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int it = 0; it < TILE_BYTES / (kThreads8 * 16); ++it) *(u32x4_t*)(vb0 + (it * kThreads8 + tid) * 16) = z;
+                for (int it = 0; it < TILE_BYTES / (kThreads8 * 16); ++it)
+                    *(u32x4_t*)(vb0 + (it * kThreads8 + tid) * 16) = z;
+            }
+            // prologue: K(0), scores of tile 0; then K(1), V(0), K(2), V(1) in flight
+            issue_k(std::false_type{}, 0, kb0, kc0);
+            __builtin_amdgcn_s_waitcnt(0xF70);
+            lds_barrier();
         }
-        // prologue: K(0), scores of tile 0; then K(1), V(0), K(2), V(1) in flight
-        issue_k(0, kb0, kc0);
-        __builtin_amdgcn_s_waitcnt(0xF70);
-        lds_barrier();
+        // (streamed: K(0), K(1) and V(0) landed before the previous block's
+        // last barrier, K(2) and V(1) are in flight)
         f32x16_t scur[2];
         scores(map ? kc0 : kb0, scur);
         mask_tile(0, scur);
         float mx_cur = tile_max(scur);
         lds_barrier();  // tile 0's K reads are done before K(3) lands in kb0
-        issue_k(min(1, n - 1), kb1, kc1);
-        issue_v(0, vb0);
-        issue_k(min(2, n - 1), kb2, kc2);
-        issue_v(min(1, n - 1), vb1);
-        wait_older_copies();
-        lds_barrier();
+        if (!pre) {
+            issue_k(std::false_type{}, 1, kb1, kc1);
+            issue_v(std::false_type{}, 0, vb0);
+            issue_k(std::false_type{}, 2, kb2, kc2);
+            issue_v(std::false_type{}, 1, vb1);
+            wait_older_copies();
+            lds_barrier();
+        }
 
         // step t: scores of t+1 from kn, P*V of t from vc; K(t+3) -> ki, V(t+2) -> vi.
         // MASKED: tile t+1 may be an edge tile of this wave (the wave-uniform
         // test in mask_tile decides); otherwise it is known to be interior for
         // every wave and the step has no mask code at all.
         // kn2, ki2: the second map's K buffers (differential attention)
-        auto step = [&](auto masked, int t, const char* kn1, const char* kn2, const char* vc, char* ki, char* ki2,
-                        char* vi) __attribute__((always_inline)) {
+        auto step = [&](auto masked, auto cross, int t, const char* kn1, const char* kn2, const char* vc, char* ki,
+                        char* ki2, char* vi) __attribute__((always_inline)) {
             constexpr bool MASKED = decltype(masked)::value;
-            issue_k(min(t + 3, n - 1), ki, ki2);
-            issue_v(min(t + 2, n - 1), vi);
+            issue_k(cross, t + 3, ki, ki2);
+            issue_v(cross, t + 2, vi);
             const char* kn = map ? kn2 : kn1;  // this wave's K buffer
             // K fragments of the next tile's first two regions; its first
             // region's scores, then this tile's head (row maximum taken in the
@@ -1120,31 +1232,57 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         int t_a = max(max(kt_hi - ((lo_key - (kTileN - 1)) >> 6), kt_hi - ((NK - kTileN) >> 6)), 0);
         int t_b = min(kt_hi - ((hi_key + kTileN - 1) >> 6), n - 1);
         if constexpr (CHUNK) t_b = min(t_b, kt_hi - ((kmin + kTileN - 1) >> 6));
-        int s1 = n, s2 = n;
+        int s1 = n3, s2 = n3;
         if (t_a <= t_b) {
-            s1 = min((max(t_a - 1, 0) + 2) / 3 * 3, n);
+            s1 = min((max(t_a - 1, 0) + 2) / 3 * 3, n3);
             s2 = s1 + max(0, t_b - s1) / 3 * 3;  // <= t_b < n; the last step's t+1 = s2 <= t_b
         }
-        auto run_masked = [&](int t0, int t1) __attribute__((always_inline)) {
+        // with a next block the last masked segment is never empty (it issues
+        // the query staging): s2 <= n3 - 3, both multiples of three
+        if (STREAM && has_next) {
+            s2 = min(s2, n3 - 3);
+            s1 = min(s1, s2);
+        }
+        // (the last segment also stages the next block's queries, waited for
+        // with its first step's older copies)
+        auto run_masked = [&](int t0, int t1, auto last) __attribute__((always_inline)) {
             for (int t = t0; t < t1; t += 3) {
                 // (already true here; stated so that the compiler's own copy
                 // tracking does not lose it at the loop head)
                 wait_older_copies();
-                step(std::true_type{}, t, kb1, kc1, vb0, kb0, kc0, vb2);
-                if (t + 1 < t1) step(std::true_type{}, t + 1, kb2, kc2, vb1, kb1, kc1, vb0);
-                if (t + 2 < t1) step(std::true_type{}, t + 2, kb0, kc0, vb2, kb2, kc2, vb1);
+                if constexpr (decltype(last)::value) {
+                    if (t == t0 && has_next) stage_q();
+                }
+                step(std::true_type{}, last, t, kb1, kc1, vb0, kb0, kc0, vb2);
+                if (t + 1 < t1) step(std::true_type{}, last, t + 1, kb2, kc2, vb1, kb1, kc1, vb0);
+                if (t + 2 < t1) step(std::true_type{}, last, t + 2, kb0, kc0, vb2, kb2, kc2, vb1);
             }
         };
-        run_masked(0, s1);
+        run_masked(0, s1, std::false_type{});
         for (int t = s1; t < s2; t += 3) {
             wait_older_copies();
-            step(std::false_type{}, t, kb1, kc1, vb0, kb0, kc0, vb2);
-            step(std::false_type{}, t + 1, kb2, kc2, vb1, kb1, kc1, vb0);
-            step(std::false_type{}, t + 2, kb0, kc0, vb2, kb2, kc2, vb1);
+            step(std::false_type{}, std::false_type{}, t, kb1, kc1, vb0, kb0, kc0, vb2);
+            step(std::false_type{}, std::false_type{}, t + 1, kb2, kc2, vb1, kb1, kc1, vb0);
+            step(std::false_type{}, std::false_type{}, t + 2, kb0, kc0, vb2, kb2, kc2, vb1);
         }
-        run_masked(s2, n);
-        // no copy may still be writing this workgroup's LDS when it ends
-        __builtin_amdgcn_s_waitcnt(0xF70);
+        if constexpr (STREAM) next_block();
+        run_masked(s2, n, std::true_type{});
+        if constexpr (STREAM) {
+            // steps n .. n3-1 (at most two, the last ones of a three-step round,
+            // so their buffers are known): copies only, which bring the next
+            // block's first tiles into the buffers its prologue would fill
+            auto copy_step = [&](int t, char* ki, char* vi) __attribute__((always_inline)) {
+                issue_k(std::true_type{}, t + 3, ki, ki);
+                issue_v(std::true_type{}, t + 2, vi);
+                wait_older_copies();
+                lds_barrier();
+            };
+            if (n3 - n == 2) copy_step(n3 - 2, kb1, vb0);
+            if (n3 - n >= 1) copy_step(n3 - 1, kb2, vb1);
+        }
+        // no copy may still be writing this workgroup's LDS when it ends (with
+        // a next block, its first copies stay in flight)
+        if (!has_next) __builtin_amdgcn_s_waitcnt(0xF70);
 
         const float lt = partner_sum(l_run);
         typedef float f32x4_t __attribute__((ext_vector_type(4)));
