@@ -358,11 +358,15 @@ band_fwd_kernel(PrefillParams p) {
         const bool edge = band ? !(j0 + kTileN - 1 <= qvw0 + wr && j0 >= qvw0 + kQw - W && j0 + kTileN <= NK)
                                : ((t - nband + 1) * kTileN > M);
         if (edge) {
-            // bit o of smask: key j0 + o is a multiple of the stride
+            // bit o of smask: key j0 + o is a multiple of the stride (or a
+            // global position).  Strided tiles: o_first is the offset of the
+            // first multiple at or after j0 (kTileN or more: none in the tile).
             uint64_t smask = 0;
+            int o_first = kTileN;
             if (STRIDED && band) {
                 const int r0 = j0 % p.stride;
-                for (int o = r0 == 0 ? 0 : p.stride - r0; o < kTileN; o += p.stride) smask |= 1ull << o;
+                o_first = r0 == 0 ? 0 : p.stride - r0;
+                for (int o = o_first; o < kTileN; o += p.stride) smask |= 1ull << o;
             }
             if (GLOBAL && band) {
                 for (int e = global_lb(j0); e < p.ng && p.gidx[e] < j0 + kTileN; ++e) smask |= 1ull << (p.gidx[e] - j0);
@@ -398,24 +402,38 @@ band_fwd_kernel(PrefillParams p) {
                         sc[kb][i] = keep_of(C) ? sc[kb][i] : -INFINITY;
                     }
             };
-            if (band && !need_hi && !need_nk) {
+            if (!band) {
+                // compact tile: entries past the list end are clamped copies
+                apply([&](int C) { return C < nk; });
+            } else if (!need_hi && !need_nk) {
                 // every key of the tile lies inside every row's window, so an
                 // extra (strided or global) key changes nothing: causal bound only
                 apply([&](int C) { return C <= lo; });
-            } else if (band && !need_lo && !need_nk) {
+            } else if (!need_lo && !need_nk) {
                 // every key is causal for every row: the window's lower
-                // bound, or an extra key below it
-                if constexpr (KEYLIST)
+                // bound, or an extra key below it.  A stride of a tile or
+                // more puts at most one multiple in the tile (at o_first), so
+                // strided tiles compare with that one key, not a bit mask.
+                if (STRIDED && p.stride >= kTileN) {
+                    if (o_first >= kTileN) {
+                        apply([&](int C) { return C > hi; });
+                    } else {
+                        int e = o_first - 8 * g;  // the multiple, as this lane's C
+                        asm volatile("" : "+v"(e));
+                        apply([&](int C) { return (C > hi) | (C == e); });
+                    }
+                } else if constexpr (KEYLIST) {
                     apply([&](int C) { return (C > hi) | (((sm >> C) & 1ull) != 0); });
-                else
+                } else {
                     apply([&](int C) { return C > hi; });
+                }
             } else {
                 // non-short-circuit operators: a straight-line select, no
                 // per-element divergent branches.  (Keys past the end exist
                 // only as clamped copies of the last row; causal rows never
                 // reach them.)
                 apply([&](int C) {
-                    return band ? (C <= lo) & (C < nk) & ((C > hi) | (KEYLIST & (((sm >> C) & 1ull) != 0))) : (C < nk);
+                    return (C <= lo) & (C < nk) & ((C > hi) | (KEYLIST & (((sm >> C) & 1ull) != 0)));
                 });
             }
         }
