@@ -108,8 +108,10 @@ int band_fwd(bool bf16, const char* name, const void* q, const void* k, const vo
     p.neg = scale < 0.f;
     p.G = (int)G;
     const int mode = diff1 ? swa::kDiff : ng > 0 ? swa::kGlobal : p.stride > 0 ? swa::kStrided : swa::kBand;
-    // one-pass differential attention: 4 query blocks x 2 maps on 8 waves
-    swa::set_wave_split(p, diff1 ? 4 : swa::waves_per_group(bf16, mode != swa::kBand, p.G, N, d), N);
+    // one-pass differential attention: 4 query blocks x 2 maps on 8 waves;
+    // key split: 2 query blocks x 2 key halves on 4 waves
+    p.ks = swa::key_split(bf16, mode, p.G) ? 1 : 0;
+    swa::set_wave_split(p, diff1 ? 4 : p.ks ? 2 : swa::waves_per_group(bf16, mode != swa::kBand, p.G, N, d), N);
     const long long total = (long long)B * Hkv * p.ngroups * p.nqb;
     if (total > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
     p.total = (int)total;

@@ -22,7 +22,9 @@
 // Structure of the 4-wave kernel (one workgroup = 4 waves = 256 threads):
 //  * A workgroup owns 4 blocks of 32 queries: HG query heads that share one
 //    KV head times PB position blocks (HG * PB = 4).  Grouped heads therefore
-//    read every K/V tile from LDS once per workgroup.
+//    read every K/V tile from LDS once per workgroup.  With the key split
+//    (bf16 local + strided, odd head groups) it owns 2 blocks, and each
+//    block's two waves take the two 32-key halves of every tile.
 //  * Key tiles of 64 rows are visited from the diagonal tile down to the
 //    lowest tile that meets the band; with stride > 0 a compact list of the
 //    strided keys below the band follows (rows gathered at j = m * stride).
@@ -118,13 +120,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
 
 // MODE: kBand (window only), kStrided (window + multiples of the stride),
 // kChunk (a chunk of new queries over the ring history plus the chunk).
-// The bf16 d = 64 strided instantiation is held to three waves per SIMD (168
-// registers; its extra mask paths would otherwise take 170, i.e. two waves):
-// short windows make most of its tiles edge tiles, and three workgroups per
-// CU hide more of each tile's latency.  The other modes run faster without
-// the cap (band and chunk at two waves; global spills under it).
-template <bool BF, int D, int MODE>
-__global__ __launch_bounds__(kThreads, (BF && D == 64 && MODE == kStrided) ? 3 : 2) void
+// KS (key split): the workgroup holds two 32-query blocks, each served by a
+// pair of waves that take the two 32-key halves of every tile with separate
+// online softmaxes, merged by their log-sum-exp at the end.  A workgroup then
+// spans 64 positions instead of 128, so with a short window each row walks
+// fewer key tiles, and each wave holds one score block instead of two.
+// The bf16 d = 64 strided instantiation without the split is held to three
+// waves per SIMD (168 registers; its extra mask paths would otherwise take
+// 170, i.e. two waves); with the split, d = 64 fits four.  The other modes
+// run faster without a cap (band and chunk at two waves; global spills under it).
+template <bool BF, int D, int MODE, bool KS = false>
+__global__ __launch_bounds__(kThreads, KS ? (D == 64 ? 4 : 2) : (BF && D == 64 && MODE == kStrided) ? 3 : 2) void
 band_fwd_kernel(PrefillParams p) {
     constexpr bool STRIDED = MODE == kStrided;
     constexpr bool CHUNK = MODE == kChunk;
@@ -142,6 +148,7 @@ band_fwd_kernel(PrefillParams p) {
     constexpr int NDB = D / 32;                      // 32-row blocks of O^T
     constexpr int KSTEP = BF ? 16 : 2;               // contraction depth per instruction
     constexpr int NQF = D / KSTEP;
+    constexpr int NKB = KS ? 1 : 2;                  // 32-key blocks of a tile per wave
     static_assert(NCH >= 1 && (kTileN * CPR) % kThreads == 0, "tile copy split");
     static_assert(VTILE_BYTES % (kThreads * 16) == 0, "V tile copy split");
 
@@ -158,6 +165,8 @@ band_fwd_kernel(PrefillParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS copy targets stay scalar
     const int g = lane >> 5, l32 = lane & 31;
+    const int half = KS ? (wave & 1) : 0;     // key half of every tile this wave takes
+    const int blk = KS ? (wave >> 1) : wave;  // 32-query block of this wave
 
     // ---- which workgroup tile is this
     const int L = xcd_remap(blockIdx.x, p.total);
@@ -185,8 +194,8 @@ band_fwd_kernel(PrefillParams p) {
     const int W = min(p.W, NK);  // a wider window reads the same keys
     const int BM = kQw * p.PB;
     const int q0 = qb * BM;
-    const int h = kvh * p.G + hg * p.HG + (wave % p.HG);
-    const int qw0 = q0 + kQw * (wave / p.HG);
+    const int h = kvh * p.G + hg * p.HG + (blk % p.HG);
+    const int qw0 = q0 + kQw * (blk / p.HG);
     const int qi = qw0 + l32;        // query row in q / out
     const int qv = qoff + qi;        // its position in the virtual sequence
     const int qvw0 = qoff + qw0;
@@ -253,12 +262,15 @@ band_fwd_kernel(PrefillParams p) {
 
     // ---- per-lane LDS bases of the fragment reads
     // K: position l32 (+32 per key half), chunk 2*cc + g (bf16) or cc/2 (fp32)
-    const int k_lane = BF ? ((((l32 >> 4) * CPR + g) << 8) + ((l32 & 15) << 4))
-                          : ((((l32 >> 4) * CPR) << 8) + ((l32 & 15) << 4) + (g << 2));
+    // (key split: the wave's 32-key block is the tile's block `half`)
+    const int k_lane = (BF ? ((((l32 >> 4) * CPR + g) << 8) + ((l32 & 15) << 4))
+                           : ((((l32 >> 4) * CPR) << 8) + ((l32 & 15) << 4) + (g << 2))) +
+                       ((half * 2 * CPR) << 8);
     // V (bf16 transpose read): row 8*g + (lane&15)/4 (+16*c2 + 4*rd),
     // element 16*((lane>>4)&1) + 4*(lane&3) (+32*db).  fp32: row 8*g, element l32.
-    const int v_lane = BF ? ((8 * g + ((lane & 15) >> 2)) * RBV + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2)
-                          : (8 * g * RBV + l32 * 4);
+    const int v_lane = (BF ? ((8 * g + ((lane & 15) >> 2)) * RBV + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2)
+                           : (8 * g * RBV + l32 * 4)) +
+                       32 * half * RBV;
 
     // ---- tile copy HBM -> LDS without registers: each wave's 16-byte
     // buffer load with the "lds" flag fills one contiguous 1 KiB block of LDS
@@ -334,7 +346,7 @@ band_fwd_kernel(PrefillParams p) {
     // kb*32 + sigma(l32), stored at position kb*32 + l32)
     auto scores = [&](const char* kl, f32x16_t* sc) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
 #pragma unroll
@@ -377,25 +389,27 @@ band_fwd_kernel(PrefillParams p) {
             // (the empty asm keeps the compiler from hoisting 32 per-lane key
             // offsets out of the tile loop instead).
             int lo, hi, nk;
+            // (key split: the wave's keys start 32 * half into the tile)
+            const int kofs = 8 * g + 32 * half;
             if (band) {
-                const int x = qv - j0 - 8 * g;
+                const int x = qv - j0 - kofs;
                 lo = x + wr;           // dist >= -wr  <=>  C <= lo
                 hi = x - W;            // dist < W     <=>  C > hi
-                nk = NK - j0 - 8 * g;  // key < NK     <=>  C < nk
+                nk = NK - j0 - kofs;   // key < NK     <=>  C < nk
             } else {
                 lo = kTileN;
                 hi = kTileN;
-                nk = M - (t - nband) * kTileN - 8 * g;  // compact entry < M
+                nk = M - (t - nband) * kTileN - kofs;  // compact entry < M
             }
             asm volatile("" : "+v"(lo), "+v"(hi), "+v"(nk));
-            const uint64_t sm = smask >> (8 * g);
+            const uint64_t sm = smask >> kofs;
             // which bounds this tile can violate (wave-uniform): most edge
             // tiles need one compare per element, not three
             const bool need_lo = j0 + kTileN - 1 > qvw0 + wr, need_nk = j0 + kTileN > NK;
             const bool need_hi = j0 < qvw0 + kQw - W;
             auto apply = [&](auto keep_of) __attribute__((always_inline)) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int C = kb * 32 + 16 * (i >> 3) + (i & 7);
@@ -418,7 +432,7 @@ band_fwd_kernel(PrefillParams p) {
                     if (o_first >= kTileN) {
                         apply([&](int C) { return C > hi; });
                     } else {
-                        int e = o_first - 8 * g;  // the multiple, as this lane's C
+                        int e = o_first - kofs;  // the multiple, as this lane's C
                         asm volatile("" : "+v"(e));
                         apply([&](int C) { return (C > hi) | (C == e); });
                     }
@@ -447,7 +461,7 @@ band_fwd_kernel(PrefillParams p) {
         // log2 domain; the lane pair (l, l^32) shares a query
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
         mx = partner_max(mx);
@@ -471,7 +485,7 @@ band_fwd_kernel(PrefillParams p) {
     auto softmax_pv = [&](f32x16_t* sc, const char* vl) __attribute__((always_inline)) {
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // row with no allowed key yet
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) sc[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], c, -m_use));
 
@@ -481,9 +495,9 @@ band_fwd_kernel(PrefillParams p) {
         float rs = 0.f;
         if constexpr (BF) {
             const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-            bf16x8_t pb[4];
+            bf16x8_t pb[2 * NKB];
 #pragma unroll
-            for (int c2 = 0; c2 < 4; ++c2) {
+            for (int c2 = 0; c2 < 2 * NKB; ++c2) {
                 // pairs are built as bf16x2 values and only whole vectors are
                 // bit-cast: extracting a dword of a bf16x8 and bit-casting it
                 // to bf16x2 mis-compiles (every pair reads element 0).
@@ -498,10 +512,10 @@ band_fwd_kernel(PrefillParams p) {
                 pb[c2] = __builtin_bit_cast(bf16x8_t, pw);
             }
 #pragma unroll
-            for (int c2 = 0; c2 < 4; ++c2)
+            for (int c2 = 0; c2 < 2 * NKB; ++c2)
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    // rows 16*c2 + 8*g + 4*rd + (lane&15)/4, 4 elements at
+                    // rows 16*c2 + 8*g + 4*rd + (lane&15)/4 (+32*half), 4 elements at
                     // d = 32*db + 16*((lane>>4)&1) + 4*(lane&3)
                     const char* vp = vl + v_lane + 16 * c2 * RBV + 64 * db;
                     const i16x4_t lo = lds_read_tr16(vp);
@@ -514,7 +528,7 @@ band_fwd_kernel(PrefillParams p) {
                 }
         } else {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     rs += sc[kb][i];
@@ -541,7 +555,7 @@ band_fwd_kernel(PrefillParams p) {
     if (ntiles > 1) issue_tile(1, kb1, vb1, true, false);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    f32x16_t scur[2];
+    f32x16_t scur[NKB];
     scores(kb0, scur);
     mask_tile(0, scur);
     __syncthreads();
@@ -550,12 +564,12 @@ band_fwd_kernel(PrefillParams p) {
         if (t + 2 < ntiles) issue_tile(t + 2, ki, vi, true, false);
         if (t + 1 < ntiles) issue_tile(t + 1, ki, vi, false, true);
         softmax_head(scur);
-        f32x16_t snext[2];
+        f32x16_t snext[NKB];
         scores(kn, snext);  // past the last tile this reads stale data and is discarded
         softmax_pv(scur, vc);
         if (t + 1 < ntiles) mask_tile(t + 1, snext);
-        scur[0] = snext[0];
-        scur[1] = snext[1];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) scur[kb] = snext[kb];
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
@@ -565,13 +579,37 @@ band_fwd_kernel(PrefillParams p) {
     }
 
     // ---- epilogue: O / l, lane holds d = 32*db + 8*quad + 4*g + 0..3
-    const float lt = partner_sum(l_run);
+    // The exponentials were taken relative to m_fin (log2 units of scale*q.k).
+    float lt = partner_sum(l_run);
+    float m_fin = (m_run == -INFINITY) ? 0.f : m_run;
+    if constexpr (KS) {
+        // The two waves of a block saw disjoint key halves: the second hands
+        // its reference max, row sum and O to the first through LDS (the
+        // loop's last barrier has freed the tile buffers), which rescales
+        // both to the larger reference and adds them.
+        float* xf = (float*)(blk == 0 ? vb0 : vb1);
+        constexpr int NO = 16 * NDB;
+        static_assert((NO + 2) * 64 * 4 <= VTILE_BYTES, "exchange fits a V buffer");
+        if (half == 1) {
+#pragma unroll
+            for (int j = 0; j < NO; ++j) xf[j * 64 + lane] = oacc[j >> 4][j & 15];
+            xf[NO * 64 + lane] = m_fin;
+            xf[(NO + 1) * 64 + lane] = lt;
+        }
+        __syncthreads();
+        if (half == 1) return;
+        const float m1 = xf[NO * 64 + lane], l1 = xf[(NO + 1) * 64 + lane];
+        const float mm = fmaxf(m_fin, m1);
+        const float a0 = __builtin_amdgcn_exp2f(m_fin - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+        lt = lt * a0 + l1 * a1;
+#pragma unroll
+        for (int j = 0; j < NO; ++j) oacc[j >> 4][j & 15] = oacc[j >> 4][j & 15] * a0 + xf[j * 64 + lane] * a1;
+        m_fin = mm;
+    }
     if (!wave_live || qi >= N) return;
     if (p.lse != nullptr && g == 0) {
-        // ln of the row's softmax denominator: the exponentials were taken
-        // relative to m_use in log2 units of scale * q.k
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        p.lse[(size_t)(b * p.Hq + h) * N + qi] = (m_use + __log2f(lt)) * 0.69314718055994531f;
+        // ln of the row's softmax denominator
+        p.lse[(size_t)(b * p.Hq + h) * N + qi] = (m_fin + __log2f(lt)) * 0.69314718055994531f;
     }
     // plain store, or (second map of differential attention) out -= lam * O/l
     const bool sub = p.lam != nullptr;
@@ -1375,6 +1413,12 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
             // including its 32-bit byte offsets into a K/V array)
             if (p.HG * p.PB == 8) {
                 hipLaunchKernelGGL((band8_kernel<D, MODE>), dim3(p.nwg), dim3(kThreads8), 0, s, p);
+                return hipGetLastError();
+            }
+        }
+        if constexpr (BF && MODE == kStrided) {
+            if (p.ks) {
+                hipLaunchKernelGGL((band_fwd_kernel<BF, D, MODE, true>), dim3(p.total), dim3(kThreads), 0, s, p);
                 return hipGetLastError();
             }
         }

@@ -39,6 +39,8 @@ struct PrefillParams {
                   // kDiff: 4, each block served by one wave per map)
     int nqb;      // query tiles per head
     int ngroups;  // G / HG
+    int ks;       // 4-wave kernel, key split: HG * PB = 2 blocks, each on a pair of
+                  // waves that take the two key halves of every tile
     int total;    // logical blocks (query tiles x head groups x KV heads x sequences)
     int nwg;      // workgroups in the grid: total, or (8-wave kernel) fewer persistent ones
 };
@@ -70,6 +72,13 @@ constexpr int kKeysPerTile = 64;
 inline int waves_per_group(bool bf16, bool keylist, int G, long long rows, int d) {
     const bool small = rows * d * 2 < (1ll << 31);
     return bf16 && !keylist && G % 2 == 0 && small ? 8 : 4;
+}
+
+// The bf16 local + strided forward with an odd number of query heads per KV
+// head runs the 4-wave kernel with its key split: two 32-query blocks per
+// workgroup (64 positions instead of 128), so each row walks fewer key tiles.
+inline bool key_split(bool bf16, int mode, int G) {
+    return bf16 && mode == kStrided && (G & 1);
 }
 
 // Split a workgroup's waves into HG query heads (of one KV head) times PB

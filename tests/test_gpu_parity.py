@@ -140,6 +140,9 @@ SHAPES = [  # (B, Hq, Hkv, N, d)
     # even head groups of more than one 8-wave workgroup: 6 per KV head (three
     # groups of 2 heads x 128 positions) and 16 (two groups of 8 heads x 32)
     (1, 12, 2, 300, 64), (1, 12, 2, 290, 128), (1, 16, 1, 280, 128), (2, 32, 2, 260, 64),
+    # odd head groups at d = 128 (bf16 strided: the 4-wave kernel's key split,
+    # two 32-query blocks per workgroup, one of them past N at the end)
+    (1, 3, 1, 150, 128), (2, 2, 2, 100, 128),
 ]
 
 
