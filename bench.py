@@ -300,12 +300,16 @@ def other_prefill_legs(swa, inputs, torch, dev, args):
 def band_kernel_name(cfg) -> str:
     """The band kernel a forward over cfg runs, by the library's routing rule:
     bf16, no extra keys (stride 0), an even number of query heads per KV head
-    and K/V arrays under 2 GiB per head take the 8-wave kernel."""
+    and K/V arrays under 2 GiB per head take the 8-wave kernel; bf16 with
+    extra keys (stride > 0) and an odd number takes the 4-wave kernel with
+    its key split."""
     bf16 = "bfloat16" in str(cfg.dtype)
     small = cfg.N * cfg.d * 2 < (1 << 31)
-    if bf16 and cfg.stride == 0 and (cfg.Hq // cfg.Hkv) % 2 == 0 and small:
+    G = cfg.Hq // cfg.Hkv
+    if bf16 and cfg.stride == 0 and G % 2 == 0 and small:
         return f"band8_kernel<d={cfg.d}, band>"
-    return f"band_fwd_kernel<{'bf16' if bf16 else 'fp32'}, d={cfg.d}, {'strided' if cfg.stride else 'band'}>"
+    split = ", key split" if bf16 and cfg.stride > 0 and G % 2 == 1 else ""
+    return f"band_fwd_kernel<{'bf16' if bf16 else 'fp32'}, d={cfg.d}, {'strided' if cfg.stride else 'band'}{split}>"
 
 
 def median(xs):

@@ -28,3 +28,10 @@ def test_gpu_count_above_one_is_refused():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True,
                        cwd=bench.ROOT)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_kernel_labels_follow_the_routing_rule():
+    from sparse_causal_attention_band_amd import inputs
+    assert bench.band_kernel_name(inputs.MISTRAL) == "band8_kernel<d=128, band>"
+    assert bench.band_kernel_name(inputs.GEMMA) == "band8_kernel<d=128, band>"
+    assert bench.band_kernel_name(inputs.STRIDED) == "band_fwd_kernel<bf16, d=64, strided, key split>"
