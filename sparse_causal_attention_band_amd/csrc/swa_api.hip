@@ -111,7 +111,8 @@ int band_fwd(bool bf16, const char* name, const void* q, const void* k, const vo
     // one-pass differential attention: 4 query blocks x 2 maps on 8 waves;
     // key split: 2 query blocks x 2 key halves on 4 waves
     p.ks = swa::key_split(bf16, mode, p.G) ? 1 : 0;
-    swa::set_wave_split(p, diff1 ? 4 : p.ks ? 2 : swa::waves_per_group(bf16, mode != swa::kBand, p.G, N, d), N);
+    const bool keylist = mode == swa::kStrided || (mode == swa::kGlobal && ng > swa::kMaxGlobal8);
+    swa::set_wave_split(p, diff1 ? 4 : p.ks ? 2 : swa::waves_per_group(bf16, keylist, p.G, N, d), N);
     const long long total = (long long)B * Hkv * p.ngroups * p.nqb;
     if (total > 0x7fffffffll) return fail(SWA_ERR_UNSUPPORTED, "%s: grid too large", name);
     p.total = (int)total;

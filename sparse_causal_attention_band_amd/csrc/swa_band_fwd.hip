@@ -700,6 +700,20 @@ __device__ __forceinline__ int persistent_block(int w, int it, int nwg, int tota
     return idx < cnt ? base + idx : -1;
 }
 
+// First entry of the sorted global-position list that is >= x (uniform
+// arguments: scalar loads).
+__device__ __forceinline__ int global_lower_bound(const int32_t* gidx, int ng, int x) {
+    int lo = 0, hi = ng;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (gidx[mid] < x)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
 __device__ __forceinline__ void lds_barrier() {
     // this wave's LDS reads done, then the workgroup barrier: no fence, so
     // the copies in flight are not drained
@@ -724,8 +738,12 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     constexpr int NQF = D / 16;                  // Q fragments
     static_assert(TILE_BYTES % 8192 == 0, "copy split");
     static_assert(NDB == NQF / 2, "one P*V instruction per score instruction");
-    static_assert(MODE == kBand || MODE == kChunk || MODE == kDiff,
-                  "band tiles only: no compact (strided or listed) keys");
+    // Global tokens: the global positions below a block's band follow its band
+    // tiles as one compact tile (the host routes lists of at most 64 positions
+    // here), and inside the band they are extra keys of the edge tiles' masks.
+    constexpr bool GLOBAL = MODE == kGlobal;
+    static_assert(MODE == kBand || MODE == kChunk || MODE == kDiff || MODE == kGlobal,
+                  "no strided keys: those take the 4-wave kernel");
 
     __shared__ __attribute__((aligned(16))) char kb0[TILE_BYTES];
     __shared__ __attribute__((aligned(16))) char kb1[TILE_BYTES];
@@ -828,7 +846,12 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         asm volatile("" ::"s"(lam_ptr), "s"(lse_ptr));
         const int kt_hi = min(NK - 1, qbase + q0 + BM - 1 + wr) / kTileN;
         const int kt_lo = max(0, qbase + q0 - W + 1) / kTileN;
-        const int ntiles = kt_hi - kt_lo + 1;
+        const int nband = kt_hi - kt_lo + 1;
+        // global mode: M global positions lie below the band (entries 0..M-1
+        // of the sorted list, the compact tile's rows)
+        int M = 0;
+        if constexpr (GLOBAL) M = global_lower_bound(p.gidx, p.ng, kt_lo * kTileN);
+        const int ntiles = GLOBAL ? nband + (M > 0 ? 1 : 0) : nband;
         const bool wave_live = qw0 < N;
         // band mode: this workgroup's next block, whose first tiles and queries
         // are copied during this block's last steps (uniform scalars)
@@ -914,6 +937,23 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             const int vr = P / RB;
             voff[it] = (uint32_t)(vr * RB + ((P % RB) ^ vswz(vr)));
         }
+        // global mode: the same lane offsets for the compact tile, whose row r
+        // is global position r of the list (rows past M repeat the last one and
+        // are masked).  The list entries are loaded here and waited for at
+        // once, so that no load of them is outstanding in the tile loop, whose
+        // copy waits count copies only.
+        uint32_t ckoff[NBLK], cvoff[NBLK];
+        if constexpr (GLOBAL) {
+#pragma unroll
+            for (int it = 0; it < NBLK; ++it) {
+                const int rk_ = (int)(koff[it] / RB), rv_ = (int)(voff[it] / RB);
+                const int gk = M > 0 ? p.gidx[min(rk_, M - 1)] : 0;
+                const int gv = M > 0 ? p.gidx[min(rv_, M - 1)] : 0;
+                ckoff[it] = (uint32_t)(min(max(gk, 0), N - 1) * RB) + koff[it] % RB;
+                cvoff[it] = (uint32_t)(min(max(gv, 0), N - 1) * RB) + voff[it] % RB;
+                asm volatile("" ::"v"(ckoff[it]), "v"(cvoff[it]));
+            }
+        }
         // The copies are buffer loads straight into LDS (MUBUF "lds" form).  A
         // resource covers one (sequence, KV head) array; the byte offset of a
         // row is a lane offset, plus a scalar tile offset when the tile's 64 rows
@@ -925,7 +965,23 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         const __amdgpu_buffer_rsrc_t rkr = CHUNK ? make_rsrc(krg, (size_t)p.W * RB) : rk;
         const __amdgpu_buffer_rsrc_t rvr = CHUNK ? make_rsrc(vrg, (size_t)p.W * RB) : rv;
         auto issue_rows = [&](int t, char* dst, const elem_t* src, __amdgpu_buffer_rsrc_t rin,
-                              __amdgpu_buffer_rsrc_t rring, const uint32_t* off) __attribute__((always_inline)) {
+                              __amdgpu_buffer_rsrc_t rring, const uint32_t* off, const uint32_t* coff)
+            __attribute__((always_inline)) {
+            if constexpr (GLOBAL) {
+                // a band tile as in band mode, or the compact tile (t = nband):
+                // per-lane rows of the whole array; source and offsets are
+                // selected, not branched on, so every step issues the same copies
+                const bool comp = t >= nband;
+                const int j0 = (kt_hi - min(t, nband - 1)) * kTileN;
+                const __amdgpu_buffer_rsrc_t rb = make_rsrc(src + (size_t)j0 * D, (size_t)(NK - j0) * RB);
+                const __amdgpu_buffer_rsrc_t r = comp ? rin : rb;
+#pragma unroll
+                for (int it = 0; it < NBLK; ++it)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        r, (__attribute__((address_space(3))) void*)(dst + (wave + 8 * it) * 1024), 16,
+                        (int)(comp ? coff[it] : off[it]), 0, 0, 0);
+                return;
+            }
             if constexpr (!CHUNK) {
                 // Band mode: one copy instruction per block whatever the tile (a
                 // branch between a contiguous and a gathered copy leaves the
@@ -989,8 +1045,8 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             } else if constexpr (STREAM) {
                 issue_band(kt_hi - min(sp, ntiles - 1), kl, kg, koff);
             } else {
-                issue_rows(min(sp, ntiles - 1), kl, kg, rk, rkr, koff);
-                if constexpr (DIFF) issue_rows(min(sp, ntiles - 1), kl2, k2g, rk, rk, koff);
+                issue_rows(min(sp, ntiles - 1), kl, kg, rk, rkr, koff, ckoff);
+                if constexpr (DIFF) issue_rows(min(sp, ntiles - 1), kl2, k2g, rk, rk, koff, ckoff);
             }
         };
         auto issue_v = [&](auto cross, int sp, char* vl) __attribute__((always_inline)) {
@@ -1000,7 +1056,7 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             } else if constexpr (STREAM) {
                 issue_band(kt_hi - min(sp, ntiles - 1), vl, vg, voff);
             } else {
-                issue_rows(min(sp, ntiles - 1), vl, vg, rv, rvr, voff);
+                issue_rows(min(sp, ntiles - 1), vl, vg, rv, rvr, voff, cvoff);
             }
         };
         // band mode: this wave's 32 query rows of the next block into its qst
@@ -1050,6 +1106,22 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             }
         };
         auto mask_tile = [&](int t, f32x16_t* sc) __attribute__((always_inline)) {
+            if constexpr (GLOBAL) {
+                if (t >= nband) {
+                    // the compact tile: element C of this lane holds entry
+                    // 8g + C, valid below M
+                    int nk = M - 8 * g;
+                    asm volatile("" : "+v"(nk));
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int C = kb * 32 + 16 * (i >> 3) + (i & 7);
+                            sc[kb][i] = C < nk ? sc[kb][i] : -INFINITY;
+                        }
+                    return;
+                }
+            }
             const int j0 = (kt_hi - t) * kTileN;
             const bool edge =
                 !(j0 + kTileN - 1 <= qvw0 + wr && j0 >= qvw0 + kQw - W && j0 + kTileN <= NK && (!CHUNK || j0 >= kmin));
@@ -1078,12 +1150,31 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
                             sc[kb][i] = keep_of(C) ? sc[kb][i] : -INFINITY;
                         }
                 };
+                // global mode: bit o of smask says key j0 + o is a global
+                // position, allowed whatever the window (tiles inside every
+                // row's window do not need it)
+                auto global_bits = [&]() __attribute__((always_inline)) {
+                    uint64_t smask = 0;
+                    for (int e = global_lower_bound(p.gidx, p.ng, j0); e < p.ng && p.gidx[e] < j0 + kTileN; ++e)
+                        smask |= 1ull << (p.gidx[e] - j0);
+                    return smask >> (8 * g);
+                };
                 if (!need_hi && !need_nk) {
                     apply([&](int C) { return C <= lo; });
                 } else if (!need_lo && !need_nk) {
-                    apply([&](int C) { return C > hi; });
+                    if constexpr (GLOBAL) {
+                        const uint64_t sm = global_bits();
+                        apply([&](int C) { return (C > hi) | (((sm >> C) & 1ull) != 0); });
+                    } else {
+                        apply([&](int C) { return C > hi; });
+                    }
                 } else {
-                    apply([&](int C) { return (C <= lo) & (C < nk) & (C > hi); });
+                    if constexpr (GLOBAL) {
+                        const uint64_t sm = global_bits();
+                        apply([&](int C) { return (C <= lo) & (C < nk) & ((C > hi) | (((sm >> C) & 1ull) != 0)); });
+                    } else {
+                        apply([&](int C) { return (C <= lo) & (C < nk) & (C > hi); });
+                    }
                 }
             }
         };
@@ -1408,9 +1499,10 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
             return hipErrorInvalidValue;
         }
     } else {
-        if constexpr (BF && (MODE == kBand || MODE == kChunk)) {
+        if constexpr (BF && (MODE == kBand || MODE == kChunk || MODE == kGlobal)) {
             // (the host picks 8 waves only where the 8-wave kernel applies,
-            // including its 32-bit byte offsets into a K/V array)
+            // including its 32-bit byte offsets into a K/V array and, for
+            // global tokens, at most 64 positions)
             if (p.HG * p.PB == 8) {
                 hipLaunchKernelGGL((band8_kernel<D, MODE>), dim3(p.nwg), dim3(kThreads8), 0, s, p);
                 return hipGetLastError();

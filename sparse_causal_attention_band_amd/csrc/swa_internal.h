@@ -60,13 +60,18 @@ hipError_t launch_ring_append(int elem_bytes, int d, const void* k, const void* 
 constexpr int kQueriesPerWave = 32;
 constexpr int kKeysPerTile = 64;
 
+// Global positions the 8-wave kernel takes: the ones below a block's band
+// form one compact tile.
+constexpr int kMaxGlobal8 = 64;
+
 // Waves per workgroup of the band kernels, which also picks the kernel (8
 // waves: the 8-wave kernel, 4: the 4-wave one).  Every wave of a workgroup
 // walks the key tiles of all its rows, so a workgroup should span few
-// positions: bf16 band and chunk modes with an even number of query heads
-// per KV head run 8 waves (4 heads x 64 positions, or 2 heads x 128), and
-// everything else (fp32, one query head per KV head, and the modes with
-// extra keys outside the window) 4 waves.  The 8-wave kernel
+// positions: bf16 band, chunk and global-token modes (at most kMaxGlobal8
+// positions) with an even number of query heads per KV head run 8 waves
+// (4 heads x 64 positions, or 2 heads x 128), and everything else (fp32,
+// odd head groups, strided keys, longer global lists: `keylist`) 4 waves.
+// The 8-wave kernel
 // addresses a K/V array with 32-bit byte offsets: `rows` (the longest K/V
 // array of one head, in rows of `d` bf16 values) must stay below 2 GiB.
 inline int waves_per_group(bool bf16, bool keylist, int G, long long rows, int d) {
