@@ -204,7 +204,19 @@ def clock_under_load(step, torch, ms_per_launch: float, launches: int = 24) -> d
             step()
         torch.cuda.synchronize()
         ms = s.elapsed_time(e)
+        # the same spin with nothing else running: the clock of an idle GPU
+        # (near the top clock if the method reads the clock, lower if the
+        # spinning wave waited for a CU)
+        icycles = int(1e7)
+        si, ei = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):
+            si.record()
+            torch.cuda._sleep(icycles)
+            ei.record()
+        torch.cuda.synchronize()
+        ims = si.elapsed_time(ei)
         return {"sclk_mhz": round(cycles / (ms * 1e-3) / 1e6, 1), "spin_cycles": cycles, "spin_ms": round(ms, 3),
+                "idle_sclk_mhz": round(icycles / (ims * 1e-3) / 1e6, 1),
                 "method": "shader cycle counter spun on a second stream during the same launches, after the timed region"}
     except Exception as ex:  # noqa: BLE001 - reported, never fatal
         return {"sclk_mhz": None, "error": f"{type(ex).__name__}: {ex}"}
@@ -278,8 +290,12 @@ def other_prefill_legs(swa, inputs, torch, dev, args):
     for cfg, steps in ((inputs.GEMMA, max(5, args.steps // 5)), (inputs.STRIDED, args.steps)):
         q, k, v = (x.to(dev) for x in inputs.prefill_inputs(cfg))
         out = torch.empty_like(q)
-        per, _ = time_launches(lambda i=0: swa.attn_fwd(q, k, v, window=cfg.window, stride=cfg.stride, out=out),
-                               steps, 10, torch)
+        fwd = lambda i=0: swa.attn_fwd(q, k, v, window=cfg.window, stride=cfg.stride, out=out)
+        per, _ = time_launches(fwd, steps, 10, torch)
+        single = median(per)
+        if cfg.stride:
+            # a launch of tens of microseconds: batches of back-to-back launches
+            per = time_batched(fwd, max(steps, 40), 0, torch)
         ms = median(per)
         fl = 4.0 * cfg.B * cfg.Hq * cfg.d * allowed_pairs(cfg.N, cfg.window, cfg.stride)
         tf = fl / (ms * 1e-3) / 1e12
@@ -287,6 +303,8 @@ def other_prefill_legs(swa, inputs, torch, dev, args):
                "median_ms": round(ms, 4), "steps": steps, "algorithmic_flops": fl,
                "kernel": band_kernel_name(cfg)}
         if cfg.stride:
+            leg.update({"timing": f"median over batches of {BATCH} back-to-back launches",
+                        "median_single_launch_ms": round(single, 4)})
             # compulsory HBM bytes: Q and O per query head, K and V per KV head
             nb = 2 * (2 * cfg.B * cfg.Hq + 2 * cfg.B * cfg.Hkv) * cfg.N * cfg.d
             leg.update({"algorithmic_bytes": nb, "GB_s": round(nb / (ms * 1e-3) / 1e9, 1),
@@ -339,6 +357,31 @@ def time_launches(fn, steps, warmup, torch, on_start=None, on_end=None):
     return per, wall
 
 
+BATCH = 8  # launches per timed batch for the short legs
+
+
+def time_batched(fn, steps, warmup, torch, batch=BATCH):
+    """Per-step times from events around batches of `batch` back-to-back
+    launches (one value per batch).  For launches of tens of microseconds,
+    events around each single launch also time the gap in which the host
+    submits the next call; a batch keeps the queue full."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    nb = max(2, steps // batch)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nb)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(nb)]
+    i = 0
+    for j in range(nb):
+        starts[j].record()
+        for _ in range(batch):
+            fn(i)
+            i += 1
+        ends[j].record()
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) / batch for s, e in zip(starts, ends)]
+
+
 def decode_leg(swa, torch, dev, dcfg, dq, dkr, dvr, dpos, steps, warmup, copies, cpu=None):
     """Time one decode step over `copies` ring copies taken in turn (so no
     step re-reads a cache-resident ring); GB/s of algorithmic bytes."""
@@ -353,7 +396,8 @@ def decode_leg(swa, torch, dev, dcfg, dq, dkr, dvr, dpos, steps, warmup, copies,
         kr_, vr_ = rings[i % copies]
         swa.decode(dqd, kr_, vr_, dposd, out=dout, workspace=ws)
 
-    dper, _ = time_launches(dstep, steps, warmup, torch)
+    single, _ = time_launches(dstep, steps, warmup, torch)
+    dper = time_batched(dstep, steps, 0, torch)
     dms = median(dper)
     n = dpos.clamp(min=0).clamp(max=W).to(torch.int64)
     dbytes = int(n.sum()) * 2 * Hkv * d * 2 + 2 * B * Hq * d * 2 + 4 * B
@@ -361,6 +405,8 @@ def decode_leg(swa, torch, dev, dcfg, dq, dkr, dvr, dpos, steps, warmup, copies,
     splits = max(1, need // (B * Hq * (d + 2) * 4)) if need else 1
     rec = {"sequences": B, "value": round(gbs, 1), "unit": "GB/s", "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
            "median_step_ms": round(dms, 4), "avg_step_ms": round(sum(dper) / len(dper), 4), "steps": steps,
+           "timing": f"median over batches of {BATCH} back-to-back steps",
+           "median_single_launch_ms": round(median(single), 4),
            "algorithmic_bytes_per_step": dbytes, "splits_per_sequence": splits, "ring_copies": copies,
            "kernels": f"decode_split_kernel<bf16,{d},{Hq // Hkv}>" +
                       (" + decode_merge_kernel" if need else " (one split: no merge kernel)")}
@@ -453,7 +499,7 @@ def main():
             swa.ring_append(ck, cv, cp0, ckr, cvr)
 
         cper, _ = time_launches(cstep, args.steps, args.warmup, torch)
-        aper, _ = time_launches(astep, args.steps, args.warmup, torch)
+        aper = time_batched(astep, max(args.steps, 40), args.warmup, torch)
         cms, ams = median(cper), median(aper)
         cpairs = sum(min(p + r + 1, ccfg.window) for p in ccfg.p0 for r in range(ccfg.T))
         cflops = 4.0 * ccfg.Hq * ccfg.d * cpairs
@@ -463,7 +509,9 @@ def main():
                          "median_launch_ms": round(cms, 4), "avg_launch_ms": round(sum(cper) / len(cper), 4),
                          "algorithmic_flops_per_launch": cflops,
                          "kernel": "band8_kernel<d=128, chunk>",
-                         "ring_append": {"median_launch_ms": round(ams, 4), "bytes": abytes,
+                         "ring_append": {"median_launch_ms": round(ams, 4),
+                                         "timing": f"median over batches of {BATCH} back-to-back launches",
+                                         "bytes": abytes,
                                          "GB_s": round(abytes / (ams * 1e-3) / 1e9, 1)}}
         del cq, ck, cv, ckr, cvr, cp0, cout
 
