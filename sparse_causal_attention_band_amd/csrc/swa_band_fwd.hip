@@ -590,17 +590,22 @@ band_fwd_kernel(PrefillParams p) {
         float* xf = (float*)(blk == 0 ? vb0 : vb1);
         constexpr int NO = 16 * NDB;
         static_assert((NO + 2) * 64 * 4 <= VTILE_BYTES, "exchange fits a V buffer");
+        // A half that met no allowed key has m_run = -inf and O = l = 0: it
+        // takes weight 0 (not exp2 of its placeholder reference 0 minus the
+        // other's max, which overflows when that max is very negative).
         if (half == 1) {
 #pragma unroll
             for (int j = 0; j < NO; ++j) xf[j * 64 + lane] = oacc[j >> 4][j & 15];
-            xf[NO * 64 + lane] = m_fin;
+            xf[NO * 64 + lane] = m_run;
             xf[(NO + 1) * 64 + lane] = lt;
         }
         __syncthreads();
         if (half == 1) return;
         const float m1 = xf[NO * 64 + lane], l1 = xf[(NO + 1) * 64 + lane];
-        const float mm = fmaxf(m_fin, m1);
-        const float a0 = __builtin_amdgcn_exp2f(m_fin - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+        const float mx = fmaxf(m_run, m1);
+        const float mm = mx == -INFINITY ? 0.f : mx;  // -inf: no allowed key in either half
+        const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+        const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
         lt = lt * a0 + l1 * a1;
 #pragma unroll
         for (int j = 0; j < NO; ++j) oacc[j >> 4][j & 15] = oacc[j >> 4][j & 15] * a0 + xf[j * 64 + lane] * a1;

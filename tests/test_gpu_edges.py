@@ -164,3 +164,24 @@ def test_key_value_arrays_beyond_2_gib():
     torch.cuda.empty_cache()
     check(torch.stack(got), np.stack(want), torch.bfloat16, "beyond 2 GiB")
     check(torch.stack(gotc), np.stack(want), torch.bfloat16, "beyond 2 GiB, chunk")
+
+
+def test_key_split_with_every_score_very_negative():
+    """bf16 local + strided with one query head per KV head runs the 4-wave
+    kernel's key split.  With every score at about -277 in log2 units, the
+    second key half of rows 0..31 meets no allowed key; merging the halves
+    must give that half weight 0 (not underflow the other half to 0/0).
+    All allowed keys have the same score, so every row is the mean of its
+    allowed V rows."""
+    say("key split, every score -192 (scale 3, q.k = -64)")
+    N, d, W, stride = 200, 64, 40, 16
+    q = torch.zeros(1, 2, N, d)
+    q[..., 0] = 8.0
+    k = torch.zeros(1, 2, N, d)
+    k[..., 0] = -8.0
+    _, _, v = inputs.random_qkv(1, 2, 2, N, d, torch.float32, seed=31)
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    out = swa.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), window=W, stride=stride, scale=3.0)
+    torch.cuda.synchronize()
+    want = oracle.attn_fwd(f64(q), f64(k), f64(v), W, stride, 3.0)
+    check(out, want, torch.bfloat16, "key split, very negative scores")
