@@ -174,8 +174,11 @@ band_fwd_kernel(PrefillParams p) {
     int rest = L / p.nqb;
     const int hg = rest % p.ngroups;
     rest /= p.ngroups;
-    const int kvh = rest % p.Hkv;
-    const int b = rest / p.Hkv;
+    // sequences inner, KV heads outer: a contiguous range of logical blocks
+    // (one XCD's) holds every sequence in equal parts, which balances the
+    // XCDs when the sequences' lengths differ (chunked prefill)
+    const int b = rest % p.B;
+    const int kvh = rest / p.B;
     const int N = p.N;
     // Chunk mode (SWA page §4.3): the N queries are chunk rows that follow
     // `start` cached positions.  They are placed at the end of a virtual
@@ -802,8 +805,8 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         int rest = L / p.nqb;
         const int hg = rest % p.ngroups;
         rest /= p.ngroups;
-        const int kvh = rest % p.Hkv;
-        const int b = rest / p.Hkv;
+        const int b = rest % p.B;  // sequences inner (see the 4-wave kernel)
+        const int kvh = rest / p.B;
         const int N = p.N;
         // Chunk mode: the virtual key sequence is [placeholders | history |
         // chunk].  The qoff = min(start, W-1) history keys come from the ring
@@ -875,7 +878,7 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             int r_n = Lx / p.nqb;
             const int hg_n = r_n % p.ngroups;
             r_n /= p.ngroups;
-            const int kvh_n = r_n % p.Hkv, b_n = r_n / p.Hkv;
+            const int b_n = r_n % p.B, kvh_n = r_n / p.B;
             const int q0_n = qb_n * BM;
             kt_hi_n = min(NK - 1, q0_n + BM - 1 + wr) / kTileN;
             n_n = kt_hi_n - max(0, q0_n - W + 1) / kTileN + 1;

@@ -41,7 +41,8 @@ struct PrefillParams {
     int ngroups;  // G / HG
     int ks;       // 4-wave kernel, key split: HG * PB = 2 blocks, each on a pair of
                   // waves that take the two key halves of every tile
-    int total;    // logical blocks (query tiles x head groups x KV heads x sequences)
+    int total;    // logical blocks (query tiles x head groups x sequences x KV heads,
+                  // the first fastest)
     int nwg;      // workgroups in the grid: total, or (8-wave kernel) fewer persistent ones
 };
 
