@@ -1467,6 +1467,39 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         if (!wave_live || qi >= N) continue;
         if (lse_ptr != nullptr && g == 0)  // ln of the row's softmax denominator (see the 4-wave kernel)
             lse_ptr[(size_t)(b * p.Hq + h) * N + qi] = (m_run + __log2f(lt)) * 0.69314718055994531f;
+        if constexpr (!DIFF) {
+            if (lam_ptr == nullptr) {
+                // Plain output, 16 bytes per lane and store: lane g of query l32
+                // holds d = 32 db + 8 quad + 4 g + 0..3.  Rounded to bf16 pairs,
+                // one cross-half swap per pair of words regroups quads 2qp and
+                // 2qp + 1 so that lane g holds d = 32 db + 16 qp + 8 g + 0..7:
+                // eight 16-byte stores per lane instead of sixteen 8-byte ones
+                // (each store instruction touches the same 32 rows either way).
+                const float inv = 1.f / lt;
+                auto pk = [&](int db, int quad, int k) __attribute__((always_inline)) {
+                    const bf16x2_t pr = {(__bf16)(oacc[db][4 * quad + 2 * k] * inv),
+                                         (__bf16)(oacc[db][4 * quad + 2 * k + 1] * inv)};
+                    return __builtin_bit_cast(uint32_t, pr);
+                };
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int qp = 0; qp < 2; ++qp) {
+                        u32x4_t w;
+#pragma unroll
+                        for (int k = 0; k < 2; ++k) {
+                            // lanes 0..31 keep quad 2qp and receive the other half's;
+                            // lanes 32..63 receive quad 2qp + 1 and keep their own
+                            const auto r = __builtin_amdgcn_permlane32_swap(pk(db, 2 * qp, k), pk(db, 2 * qp + 1, k),
+                                                                            false, false);
+                            w[k] = r[0];
+                            w[2 + k] = r[1];
+                        }
+                        *(u32x4_t*)(og + (size_t)qi * D + 32 * db + 16 * qp + 8 * g) = w;
+                    }
+                continue;
+            }
+        }
         // second launch of the two-launch differential attention: out -= lam * O/l
         const bool sub = !DIFF && lam_ptr != nullptr;
         const float inv = (sub ? -lam_ptr[h] : 1.f) / lt;
