@@ -619,7 +619,34 @@ band_fwd_kernel(PrefillParams p) {
         // ln of the row's softmax denominator
         p.lse[(size_t)(b * p.Hq + h) * N + qi] = (m_fin + __log2f(lt)) * 0.69314718055994531f;
     }
-    // plain store, or (second map of differential attention) out -= lam * O/l
+    if constexpr (BF) {
+        if (p.lam == nullptr) {
+            // plain bf16 output, 16 bytes per store: one swap between the two
+            // lanes of a query (both active or both not) per pair of words
+            // regroups quads 2qp and 2qp + 1 so that lane g holds
+            // d = 32 db + 16 qp + 8 g + 0..7 (as in the 8-wave kernel)
+            const float inv = 1.f / lt;
+            auto pk = [&](int db, int quad, int k) __attribute__((always_inline)) {
+                const bf16x2_t pr = {(__bf16)(oacc[db][4 * quad + 2 * k] * inv), (__bf16)(oacc[db][4 * quad + 2 * k + 1] * inv)};
+                return __builtin_bit_cast(uint32_t, pr);
+            };
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int qp = 0; qp < 2; ++qp) {
+                    u32x4_t w;
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const auto r = __builtin_amdgcn_permlane32_swap(pk(db, 2 * qp, k), pk(db, 2 * qp + 1, k), false, false);
+                        w[k] = r[0];
+                        w[2 + k] = r[1];
+                    }
+                    *(u32x4_t*)(og + (size_t)qi * D + 32 * db + 16 * qp + 8 * g) = w;
+                }
+            return;
+        }
+    }
+    // plain store (fp32), or (second map of differential attention) out -= lam * O/l
     const bool sub = p.lam != nullptr;
     const float inv = (sub ? -p.lam[h] : 1.f) / lt;
 #pragma unroll
