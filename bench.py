@@ -193,7 +193,11 @@ def clock_under_load(step, torch, ms_per_launch: float, launches: int = 24) -> d
         side = torch.cuda.Stream()
         for _ in range(3):
             step()
-        # spin for about 60 % of the queued work at ~2 GHz
+        # The spin starts on an idle GPU, so that its wave is placed at once
+        # (queued behind launches that hold every CU, its event interval would
+        # also count the wait for a slot), then the launches follow it; it
+        # spins for about 60 % of their work at ~2 GHz.
+        torch.cuda.synchronize()
         cycles = int(max(2e6, 0.6 * launches * ms_per_launch * 1e-3 * 2.0e9))
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(side):
