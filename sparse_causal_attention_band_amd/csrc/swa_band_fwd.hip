@@ -13,11 +13,12 @@
 // enumerates only key tiles that meet the band.
 //
 // Two kernels share the tile enumeration, layouts, masking and softmax: the
-// 8-wave bf16 kernel at the end of this file (band and chunk modes with an
-// even number of query heads per KV head) and the 4-wave kernel described
-// here (fp32, the strided and global modes, one or an odd number of query
-// heads per KV head, and K/V arrays of 2 GiB or more per head, which the
-// 8-wave kernel's 32-bit byte offsets cannot address).
+// 8-wave bf16 kernel at the end of this file (band, chunk and global-token
+// modes with an even number of query heads per KV head, global lists of at
+// most 64 positions, and one-pass differential attention) and the 4-wave
+// kernel described here (fp32, the strided mode, longer global lists, one or
+// an odd number of query heads per KV head, and K/V arrays of 2 GiB or more
+// per head, which the 8-wave kernel's 32-bit byte offsets cannot address).
 //
 // Structure of the 4-wave kernel (one workgroup = 4 waves = 256 threads):
 //  * A workgroup owns 4 blocks of 32 queries: HG query heads that share one
@@ -707,7 +708,15 @@ band_fwd_kernel(PrefillParams p) {
 //  * the copies are buffer loads into LDS rather than global-segment loads:
 //    the latter are FLAT instructions that may also address LDS, and with
 //    one in flight the compiler's wait counting can no longer wait for a
-//    single LDS read (every wait in the loop became a full drain).
+//    single LDS read (every wait in the loop became a full drain);
+//  * a block's steps run in three segments, masked, mask-free and masked,
+//    so that the tiles inside every row's band go through a loop with no
+//    mask code and no branch;
+//  * the grid is persistent, one workgroup per CU running its blocks in
+//    turn, and in band mode a block's last steps already copy the next
+//    block's first tiles and stage its queries in LDS;
+//  * the output of each query is regrouped between its two lanes so that a
+//    lane stores 16 consecutive bytes at a time.
 constexpr int kThreads8 = 512;
 
 // Raw buffer resource over [base, base + bytes): stride 0, bounds checked
