@@ -126,12 +126,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
 // online softmaxes, merged by their log-sum-exp at the end.  A workgroup then
 // spans 64 positions instead of 128, so with a short window each row walks
 // fewer key tiles, and each wave holds one score block instead of two.
-// The bf16 d = 64 strided instantiation without the split is held to three
-// waves per SIMD (168 registers; its extra mask paths would otherwise take
-// 170, i.e. two waves); with the split, d = 64 fits four.  The other modes
-// run faster without a cap (band and chunk at two waves; global spills under it).
+// With the split, d = 64 fits four workgroups per CU (120 registers); every
+// other instantiation runs two (a cap of three spilled in the strided and
+// global modes).
 template <bool BF, int D, int MODE, bool KS = false>
-__global__ __launch_bounds__(kThreads, KS ? (D == 64 ? 4 : 2) : (BF && D == 64 && MODE == kStrided) ? 3 : 2) void
+__global__ __launch_bounds__(kThreads, KS && D == 64 ? 4 : 2) void
 band_fwd_kernel(PrefillParams p) {
     constexpr bool STRIDED = MODE == kStrided;
     constexpr bool CHUNK = MODE == kChunk;
