@@ -823,6 +823,12 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
     // blocks, and the code of the block loop stays in the instruction cache.
     // (the one-pass differential mode keeps one block per workgroup: the
     // block loop would push its registers past the budget)
+    // A block's queries and its first tile's scores.  In band mode, blocks
+    // after a workgroup's first get both from the previous block's last step
+    // (the one whose score block would otherwise be discarded), so their
+    // prologue only masks and takes the row maximum.
+    bf16x8_t qf[NQF];
+    f32x16_t scur[2];
     for (int iter = 0;; ++iter) {
         if (DIFF && iter > 0) break;
         const int L = DIFF ? xcd_remap(blockIdx.x, p.total) : persistent_block(blockIdx.x, iter, p.nwg, p.total);
@@ -830,8 +836,9 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         // Band mode: the previous block's last steps already copied this
         // block's first K and V tiles into the buffers its prologue would fill
         // and staged its queries (its tile list is padded to a multiple of
-        // three steps, so the buffer rotation continues unchanged), so the
-        // prologue only computes the first tile's scores.  Other modes: the
+        // three steps, so the buffer rotation continues unchanged), and its
+        // last step loaded them and computed the first tile's scores, so the
+        // prologue only masks that tile and has no barrier.  Other modes: the
         // previous block's waves are done with every LDS buffer (and every
         // copy has landed) before this block's prologue writes them.
         const bool pre = STREAM && iter > 0;
@@ -927,27 +934,15 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         // steps that only copy, up to a multiple of three
         const int n3 = has_next ? (ntiles + 2) / 3 * 3 : ntiles;
 
-        bf16x8_t qf[NQF];
-        {
+        if (!pre) {
             const uint32_t flip = p.neg ? 0x80008000u : 0u;
             const uint32_t keep = qi < N ? 0xffffffffu : 0u;
             const size_t qrow = (size_t)min(qi, N - 1) * D;
-            if (pre) {
-                // staged by the previous block: chunk 2c + g of row l32
-                const char* qs = (wave < 4 ? (wave < 2 ? qs0 : qs1) : (wave < 6 ? qs2 : qs3)) + (wave & 1) * (kQw * RB);
 #pragma unroll
-                for (int c = 0; c < NQF; ++c) {
-                    u32x4_t w = *(const u32x4_t*)(qs + (((2 * c + g) * kQw + l32) << 4));
-                    w = (w & keep) ^ flip;
-                    qf[c] = __builtin_bit_cast(bf16x8_t, w);
-                }
-            } else {
-#pragma unroll
-                for (int c = 0; c < NQF; ++c) {
-                    u32x4_t w = *(const u32x4_t*)(qg + qrow + 16 * c + 8 * g);
-                    w = (w & keep) ^ flip;
-                    qf[c] = __builtin_bit_cast(bf16x8_t, w);
-                }
+            for (int c = 0; c < NQF; ++c) {
+                u32x4_t w = *(const u32x4_t*)(qg + qrow + 16 * c + 8 * g);
+                w = (w & keep) ^ flip;
+                qf[c] = __builtin_bit_cast(bf16x8_t, w);
             }
         }
 
@@ -1115,6 +1110,22 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
                         r, (__attribute__((address_space(3))) void*)(qs + b4 * 1024), 16,
                         l32 * RB + ((2 * b4 + g) << 4), 0, 0, 0);
+            }
+        };
+        // band mode: the next block's queries from the staging area into qf
+        // (chunk 2c + g of row l32), at the last step of this block's list.
+        // Rows past the sequence arrive as zeros (the staging copy's range
+        // check), so only a negative scale needs a pass over the registers.
+        auto load_next_q = [&]() __attribute__((always_inline)) {
+            if constexpr (STREAM) {
+                const char* qs = (wave < 4 ? (wave < 2 ? qs0 : qs1) : (wave < 6 ? qs2 : qs3)) + (wave & 1) * (kQw * RB);
+#pragma unroll
+                for (int c = 0; c < NQF; ++c) qf[c] = *(const bf16x8_t*)(qs + (((2 * c + g) * kQw + l32) << 4));
+                if (p.neg) {
+#pragma unroll
+                    for (int c = 0; c < NQF; ++c)
+                        qf[c] = __builtin_bit_cast(bf16x8_t, __builtin_bit_cast(u32x4_t, qf[c]) ^ 0x80008000u);
+                }
             }
         };
         // Every step issues the same copies (past the end of the list the last
@@ -1355,12 +1366,14 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             lds_barrier();
         }
         // (streamed: K(0), K(1) and V(0) landed before the previous block's
-        // last barrier, K(2) and V(1) are in flight)
-        f32x16_t scur[2];
-        scores(map ? kc0 : kb0, scur);
+        // last barrier, K(2) and V(1) are in flight, and that block's last step
+        // already computed tile 0's scores from K(0) with these queries)
+        if (!pre) scores(map ? kc0 : kb0, scur);
         mask_tile(0, scur);
         float mx_cur = tile_max(scur);
-        lds_barrier();  // tile 0's K reads are done before K(3) lands in kb0
+        // tile 0's K reads are done before K(3) lands in kb0 (streamed: they
+        // were done before the previous block's last barrier)
+        if (!pre) lds_barrier();
         if (!pre) {
             issue_k(std::false_type{}, 1, kb1, kc1);
             issue_v(std::false_type{}, 0, vb0);
@@ -1375,9 +1388,16 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
         // test in mask_tile decides); otherwise it is known to be interior for
         // every wave and the step has no mask code at all.
         // kn2, ki2: the second map's K buffers (differential attention)
-        auto step = [&](auto masked, auto cross, int t, const char* kn1, const char* kn2, const char* vc, char* ki,
-                        char* ki2, char* vi) __attribute__((always_inline)) {
+        // LASTPOS: the step may be the list's last position (a round's third
+        // step of the last segment, as n3 is a multiple of three), whose score
+        // block becomes the next block's first (tile 0 from K(0) in kb0, with
+        // the next block's queries)
+        auto step = [&](auto masked, auto cross, auto lastpos, int t, const char* kn1, const char* kn2, const char* vc,
+                        char* ki, char* ki2, char* vi) __attribute__((always_inline)) {
             constexpr bool MASKED = decltype(masked)::value;
+            if constexpr (STREAM && decltype(lastpos)::value) {
+                if (has_next && t == n3 - 1) load_next_q();
+            }
             issue_k(cross, t + 3, ki, ki2);
             issue_v(cross, t + 2, vi);
             const char* kn = map ? kn2 : kn1;  // this wave's K buffer
@@ -1443,17 +1463,17 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
                 if constexpr (decltype(last)::value) {
                     if (t == t0 && has_next) stage_q();
                 }
-                step(std::true_type{}, last, t, kb1, kc1, vb0, kb0, kc0, vb2);
-                if (t + 1 < t1) step(std::true_type{}, last, t + 1, kb2, kc2, vb1, kb1, kc1, vb0);
-                if (t + 2 < t1) step(std::true_type{}, last, t + 2, kb0, kc0, vb2, kb2, kc2, vb1);
+                step(std::true_type{}, last, std::false_type{}, t, kb1, kc1, vb0, kb0, kc0, vb2);
+                if (t + 1 < t1) step(std::true_type{}, last, std::false_type{}, t + 1, kb2, kc2, vb1, kb1, kc1, vb0);
+                if (t + 2 < t1) step(std::true_type{}, last, last, t + 2, kb0, kc0, vb2, kb2, kc2, vb1);
             }
         };
         run_masked(0, s1, std::false_type{});
         for (int t = s1; t < s2; t += 3) {
             wait_older_copies();
-            step(std::false_type{}, std::false_type{}, t, kb1, kc1, vb0, kb0, kc0, vb2);
-            step(std::false_type{}, std::false_type{}, t + 1, kb2, kc2, vb1, kb1, kc1, vb0);
-            step(std::false_type{}, std::false_type{}, t + 2, kb0, kc0, vb2, kb2, kc2, vb1);
+            step(std::false_type{}, std::false_type{}, std::false_type{}, t, kb1, kc1, vb0, kb0, kc0, vb2);
+            step(std::false_type{}, std::false_type{}, std::false_type{}, t + 1, kb2, kc2, vb1, kb1, kc1, vb0);
+            step(std::false_type{}, std::false_type{}, std::false_type{}, t + 2, kb0, kc0, vb2, kb2, kc2, vb1);
         }
         if constexpr (STREAM) next_block();
         run_masked(s2, n, std::true_type{});
@@ -1461,14 +1481,22 @@ __global__ __launch_bounds__(kThreads8, D == 64 ? 2 : 1) void band8_kernel(Prefi
             // steps n .. n3-1 (at most two, the last ones of a three-step round,
             // so their buffers are known): copies only, which bring the next
             // block's first tiles into the buffers its prologue would fill
-            auto copy_step = [&](int t, char* ki, char* vi) __attribute__((always_inline)) {
+            // (the list's last position computes the next block's tile 0
+            // scores, as a tile step there would)
+            auto copy_step = [&](auto last_pos, int t, char* ki, char* vi) __attribute__((always_inline)) {
+                if constexpr (decltype(last_pos)::value) {
+                    if (has_next) {
+                        load_next_q();
+                        scores(kb0, scur);
+                    }
+                }
                 issue_k(std::true_type{}, t + 3, ki, ki);
                 issue_v(std::true_type{}, t + 2, vi);
                 wait_older_copies();
                 lds_barrier();
             };
-            if (n3 - n == 2) copy_step(n3 - 2, kb1, vb0);
-            if (n3 - n >= 1) copy_step(n3 - 1, kb2, vb1);
+            if (n3 - n == 2) copy_step(std::false_type{}, n3 - 2, kb1, vb0);
+            if (n3 - n >= 1) copy_step(std::true_type{}, n3 - 1, kb2, vb1);
         }
         // no copy may still be writing this workgroup's LDS when it ends (with
         // a next block, its first copies stay in flight)

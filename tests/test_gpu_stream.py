@@ -3,8 +3,10 @@ query blocks and streams from one into the next (shapes with more query
 blocks than CUs): every output element against the float64 oracle, in
 NaN-filled buffers.  Cases: ragged sequence ends, windows of one key (blocks
 with fewer than three tiles, padded with copy-only steps), 2, 4 and 8 query
-heads per KV head, the two-sided band, the row log-sum-exp, and blocks whose
-successor lies in another head or sequence.  Tolerances as in the other
+heads per KV head, the two-sided band, a negative scale (the sign enters
+through the queries, also those a block takes over from its predecessor's
+staging), the row log-sum-exp, and blocks whose successor lies in another
+head or sequence.  Tolerances as in the other
 parity tests (bf16: 1.5e-2 max, 1e-3 mean; log-sum-exp 2.5e-3).  Each case
 prints its parameters before it touches the GPU."""
 import math
@@ -45,31 +47,33 @@ def _compare(got, want_of, B, Hq, what, tol=1.5e-2):
     return st
 
 
-# (B, Hq, Hkv, N, d, window, right)
+# (B, Hq, Hkv, N, d, window, right, scale; 0: 1/sqrt(d))
 CASES = [
-    (1, 8, 2, 32768 - 37, 128, 100, 0),    # 4 heads per KV head, ragged end, 1024 blocks
-    (2, 4, 2, 16384 + 5, 64, 1, 0),        # 2 heads per KV head, one key: blocks of 1-2 tiles
-    (1, 16, 2, 20000, 128, 700, 0),        # 8 heads per KV head: 32-row blocks
-    (3, 8, 4, 5000, 128, 64, 0),           # successors in other heads and sequences
-    (1, 8, 2, 20000, 128, 201, 150),       # two-sided band
+    (1, 8, 2, 32768 - 37, 128, 100, 0, 0),    # 4 heads per KV head, ragged end, 1024 blocks
+    (2, 4, 2, 16384 + 5, 64, 1, 0, 0),        # 2 heads per KV head, one key: blocks of 1-2 tiles
+    (1, 16, 2, 20000, 128, 700, 0, 0),        # 8 heads per KV head: 32-row blocks
+    (3, 8, 4, 5000, 128, 64, 0, 0),           # successors in other heads and sequences
+    (1, 8, 2, 20000, 128, 201, 150, 0),       # two-sided band
+    (2, 8, 2, 9000 + 3, 128, 150, 0, -0.11),  # negative scale, 564 blocks, ragged end
+    (1, 8, 4, 17000, 64, 64, 0, -0.2),        # negative scale, d = 64, 532 blocks
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_Hq{}_Hkv{}_N{}_d{}_W{}_r{}".format(*c))
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_Hq{}_Hkv{}_N{}_d{}_W{}_r{}_s{}".format(*c))
 def test_streamed_blocks_match_oracle(case):
-    B, Hq, Hkv, N, d, W, right = case
+    B, Hq, Hkv, N, d, W, right, sc = case
     say(f"streamed band {case}")
     q, k, v = inputs.random_qkv(B, Hq, Hkv, N, d, torch.bfloat16, seed=N % 1000 + W)
+    G, scale = Hq // Hkv, sc if sc else 1 / math.sqrt(d)
     out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
     if right:
-        swa.attn_fwd_two_sided(q.to(DEV), k.to(DEV), v.to(DEV), W - 1, right, out=out)
+        swa.attn_fwd_two_sided(q.to(DEV), k.to(DEV), v.to(DEV), W - 1, right, scale=scale, out=out)
     else:
-        swa.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), window=W, out=out)
+        swa.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), window=W, scale=scale, out=out)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     del out
     qf, kf, vf = q.float().numpy(), k.float().numpy(), v.float().numpy()
-    G, scale = Hq // Hkv, 1 / math.sqrt(d)
 
     def want(bh):
         b, h = bh
