@@ -5,8 +5,8 @@ NaN-filled buffers.  Cases: ragged sequence ends, windows of one key (blocks
 with fewer than three tiles, padded with copy-only steps), 2, 4 and 8 query
 heads per KV head, the two-sided band, a negative scale (the sign enters
 through the queries, also those a block takes over from its predecessor's
-staging), the row log-sum-exp, and blocks whose successor lies in another
-head or sequence.  Tolerances as in the other
+staging), the row log-sum-exp, blocks whose successor lies in another head
+or sequence, and seeded random shapes of the same kind.  Tolerances as in the other
 parity tests (bf16: 1.5e-2 max, 1e-3 mean; log-sum-exp 2.5e-3).  Each case
 prints its parameters before it touches the GPU."""
 import math
@@ -104,3 +104,50 @@ def test_streamed_blocks_lse():
     st = _compare(got, lambda bh: oracle.attn_lse(qf[:, bh[1]:bh[1] + 1], kf[:, bh[1] // G:bh[1] // G + 1], W, 0,
                                                   scale)[0, 0], B, Hq, "lse", tol=2.5e-3)
     assert st.nonfinite == 0 and st.over == 0, (st.max_err, st.worst)
+
+
+def _random_stream_case(i):
+    """Seeded random shape with more query blocks than workgroups (case i)."""
+    rng = np.random.default_rng(777000 + i)
+    d = int(rng.choice([64, 128]))
+    G = int(rng.choice([2, 4, 6, 8]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    B = int(rng.integers(1, 3))
+    N = int(rng.integers(4000, 14001))
+    # a window of one key or of at least 16 (smaller ones return near-copies
+    # of V rows, which the flat bf16 bound does not cover)
+    W = int(rng.choice([1, int(rng.integers(16, 1500))]))
+    right = int(rng.choice([0, 0, 0, int(rng.integers(1, 400))]))
+    scale = (1 / math.sqrt(d)) * float(rng.choice([1.0, 1.0, -1.0, 0.5]))
+    return B, G * Hkv, Hkv, N, d, W, right, scale
+
+
+@pytest.mark.parametrize("i", [1, 2, 4, 13, 17, 22])
+def test_streamed_random_shapes(i):
+    """Random shapes through the streamed path (ragged ends, 2-8 query heads
+    per KV head, d 64 and 128, two-sided bands, negative scales), every output
+    element against the oracle."""
+    B, Hq, Hkv, N, d, W, right, scale = _random_stream_case(i)
+    say(f"streamed random {i}: B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} W{W} right{right} scale{scale:.4f}")
+    q, k, v = inputs.random_qkv(B, Hq, Hkv, N, d, torch.bfloat16, seed=i + 99)
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
+    if right:
+        swa.attn_fwd_two_sided(q.to(DEV), k.to(DEV), v.to(DEV), W - 1, right, scale=scale, out=out)
+    else:
+        swa.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), window=W, scale=scale, out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    del out
+    qf, kf, vf = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    G = Hq // Hkv
+
+    def want(bh):
+        b, h = bh
+        g = slice(h // G, h // G + 1)
+        if right:
+            return oracle.attn_fwd_two_sided(qf[b:b + 1, h:h + 1], kf[b:b + 1, g], vf[b:b + 1, g], W - 1, right,
+                                             scale)[0, 0]
+        return oracle.attn_fwd(qf[b:b + 1, h:h + 1], kf[b:b + 1, g], vf[b:b + 1, g], W, 0, scale)[0, 0]
+
+    st = _compare(got, want, B, Hq, f"random {i}")
+    full_parity.assert_bf16(st, f"random {i}")
