@@ -295,7 +295,7 @@ SWA_API size_t swa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int win
  *   partials: calls that may overlap on one GPU (different streams, or one
  *   stream and a graph replay) race and must be serialised by the caller.
  */
-#define SWA_DECODE_NOALLOC_SCRATCH_BYTES 4259840
+#define SWA_DECODE_NOALLOC_SCRATCH_BYTES 2129920
 SWA_API int swa_decode_noalloc(const void* q, const void* kring, const void* vring, const int32_t* pos,
                                void* out, int B, int Hq, int Hkv, int d, float scale, int window,
                                hipStream_t stream);

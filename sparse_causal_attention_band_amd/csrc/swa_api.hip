@@ -317,9 +317,9 @@ int ring_append(bool bf16, const void* k, const void* v, const int32_t* p0, void
 
 // Scratch of the allocation-free decode entry point: the split partials
 // ([B, Hq, nsplit, d] sums, then [B, Hq, nsplit, 2] (max, sum)).  The split
-// plan splits only below 512 (sequence, KV head) pairs, so pairs x splits
-// stays under 1024 and the partials under 8 heads per KV head x 1022 x
-// (128 + 2) floats.  Each GPU holds its own copy; host code never names the
+// plan splits only below 256 (sequence, KV head) pairs, so pairs x splits
+// stays under 512 (at most 255 x 2) and the partials under 8 heads per KV
+// head x 510 x (128 + 2) floats.  Each GPU holds its own copy; host code never names the
 // array itself (on the host the name is only a handle), it uses the device
 // address looked up once per device.
 constexpr size_t kNoAllocScratchBytes = SWA_DECODE_NOALLOC_SCRATCH_BYTES;

@@ -430,7 +430,11 @@ hipError_t launch_decode(bool bf16, int d, int G, const DecodeParams& p, hipStre
 
 DecodeSplit decode_split_plan(int B, int Hkv, int W) {
     const long long pairs = (long long)B * Hkv;      // (sequence, KV head) pairs
-    const long long want = 512;                       // two workgroups per CU
+    // one workgroup per CU: with fewer (sequence, KV head) pairs than CUs the
+    // slots split until the pairs x splits workgroups fill them; more splits
+    // (two or four workgroups per CU) measured slower on 4-32 sequences, the
+    // extra partials and merge work outweighing the shorter streams
+    const long long want = 256;
     const int tiles = (W + kTile - 1) / kTile;
     long long ns = pairs >= want ? 1 : (want + pairs - 1) / pairs;
     if (ns > tiles) ns = tiles;
