@@ -713,7 +713,8 @@ band_fwd_kernel(PrefillParams p) {
 //    mask code and no branch;
 //  * the grid is persistent, one workgroup per CU running its blocks in
 //    turn, and in band mode a block's last steps already copy the next
-//    block's first tiles and stage its queries in LDS;
+//    block's first tiles and stage its queries in LDS, and its last step
+//    computes the next block's first score block;
 //  * the output of each query is regrouped between its two lanes so that a
 //    lane stores 16 consecutive bytes at a time.
 constexpr int kThreads8 = 512;
