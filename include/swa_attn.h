@@ -121,10 +121,10 @@ SWA_API int swa_attn_fwd_lse_f32(const float* q, const float* k, const float* v,
  *                  When that size is 0 the pointer is not used (may be NULL).
  *   Hq / Hkv must be 1, 2, 4 or 8; d in {64, 128}; window >= 1.
  * One workgroup streams the K/V slots of one (sequence, KV head) pair from
- * HBM and serves its Hq/Hkv query heads.  With fewer than 512 such pairs the
- * slots are split so the GPU still gets two workgroups per CU: each split
+ * HBM and serves its Hq/Hkv query heads.  With fewer than 256 such pairs the
+ * slots are split so the GPU still gets one workgroup per CU: each split
  * writes (max, sum, weighted V) partials into the workspace and a second
- * kernel merges them by log-sum-exp; with 512 or more pairs there is one
+ * kernel merges them by log-sum-exp; with 256 or more pairs there is one
  * kernel and no workspace.
  */
 SWA_API int swa_decode(const void* q, const void* kring, const void* vring, const int32_t* pos,

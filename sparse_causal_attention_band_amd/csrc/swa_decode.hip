@@ -8,11 +8,11 @@
 // order; which slots are valid is all that depends on pos.
 //
 // The step is bound by HBM bandwidth (about 4 flops per byte), so it is split
-// along the slots ("split-K") only as far as needed to give every CU two
-// workgroups: grid = (splits, KV heads, sequences), each workgroup streams
+// along the slots ("split-K") only as far as needed to give every CU one
+// workgroup: grid = (splits, KV heads, sequences), each workgroup streams
 // its slots of one KV head in 64-slot tiles and serves all G query heads of
 // that KV head, so every K/V byte is read from HBM once.  With one split
-// (512 or more (sequence, KV head) pairs) the workgroup writes the output
+// (256 or more (sequence, KV head) pairs) the workgroup writes the output
 // itself.  The kernel is a pure register stream:
 //   * 16-byte chunks per lane, a ring row of d elements spread over CPR
 //     consecutive lanes: a 256-byte bf16 row over 8 lanes with two chunks

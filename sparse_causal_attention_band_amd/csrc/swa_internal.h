@@ -121,7 +121,7 @@ struct DecodeParams {
     int neg;
 };
 
-// Split plan: enough workgroups for two per CU (256 CUs), each split a whole
+// Split plan: enough workgroups for one per CU (256 CUs), each split a whole
 // number of 64-slot tiles.  One split means no workspace and no merge kernel.
 struct DecodeSplit {
     int nsplit;

@@ -86,10 +86,10 @@ def test_decode_rejects_bad_arguments(kw, code):
 
 def test_workspace_size_formula():
     L = swa.lib()
-    # 512 or more (sequence, KV head) pairs: one split, no workspace
+    # 256 or more (sequence, KV head) pairs: one split, no workspace
     assert L.swa_decode_workspace_bytes(64, 32, 8, 128, 4096) == 0
     assert L.swa_decode_workspace_bytes(1, 1, 1, 64, 1) == 0  # a single 64-slot tile cannot split
-    # otherwise ceil(512 / pairs) splits of whole 64-slot tiles, each holding
+    # otherwise ceil(256 / pairs) splits of whole 64-slot tiles, each holding
     # d floats + (max, sum) per (sequence, query head)
     assert L.swa_decode_workspace_bytes(1, 1, 1, 64, 513) == 9 * 66 * 4       # 9 tiles, 9 splits
     assert L.swa_decode_workspace_bytes(10, 32, 8, 128, 4096) == 10 * 32 * 4 * 130 * 4  # 80 pairs -> 4 splits

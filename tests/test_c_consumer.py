@@ -35,7 +35,7 @@ int main(void) {
                   SWA_ERR_INVALID_ARG, "swa_attn_fwd_lse");
     bad |= expect(swa_decode(a, a, a, NULL, a, 2, 8, 2, 128, 0.1f, NULL, 0, 4096, NULL), SWA_ERR_INVALID_ARG,
                   "swa_decode");
-    /* 512 (sequence, KV head) pairs: one split, no workspace; 4 pairs: split */
+    /* 512 (sequence, KV head) pairs (256 or more): one split, no workspace; 4 pairs: split */
     if (swa_decode_workspace_bytes(64, 32, 8, 128, 4096) != 0) bad = 1;
     if (swa_decode_workspace_bytes(2, 8, 2, 128, 4096) == 0) bad = 1;
     printf(bad ? "FAILED\n" : "OK\n");
