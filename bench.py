@@ -226,6 +226,86 @@ def clock_under_load(step, torch, ms_per_launch: float, launches: int = 24) -> d
         return {"sclk_mhz": None, "error": f"{type(ex).__name__}: {ex}"}
 
 
+def smi_clock_under_load(step, torch, ms_per_launch: float, seconds: float = 3.0) -> dict:
+    """The graphics clock of every XCD while `step` (the timed launch) runs
+    back to back, from the management library's metrics table (amdsmi).  The
+    table refreshes about once a second, so the launches run for `seconds`
+    and only samples taken from 1.2 s on count, and only if they differ from
+    the reading before the launches (else the table did not refresh).  Run
+    after the timed region.  {} when the library or the device is not there."""
+    import threading
+
+    try:
+        import amdsmi
+    except Exception:  # noqa: BLE001 - optional
+        return {}
+    try:
+        amdsmi.amdsmi_init()
+    except Exception as ex:  # noqa: BLE001 - reported, never fatal
+        return {"error": f"amdsmi_init: {type(ex).__name__}: {ex}"}
+    try:
+        hs = amdsmi.amdsmi_get_processor_handles()
+        h = None
+        if len(hs) == 1:
+            h = hs[0]
+        else:
+            props = torch.cuda.get_device_properties(0)
+            bus = getattr(props, "pci_bus_id", None)
+            for c in hs:
+                bdf = str(amdsmi.amdsmi_get_gpu_device_bdf(c))  # dddd:bb:dd.f
+                if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                    h = c
+                    break
+        if h is None:
+            return {"error": "no management-library handle matched the device"}
+
+        def read():
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            xs = m.get("current_gfxclks")
+            if isinstance(xs, (list, tuple)):
+                xs = [int(x) for x in xs if isinstance(x, (int, float)) and 0 < x < 65535]
+            if not xs:
+                c = m.get("current_gfxclk")
+                xs = [int(c)] if isinstance(c, (int, float)) and 0 < c < 65535 else []
+            return xs
+
+        before = read()
+        samples = []
+        stop = threading.Event()
+
+        def sampler(t0):
+            while not stop.is_set():
+                samples.append((time.perf_counter() - t0, read()))
+                time.sleep(0.02)
+
+        batch = max(1, int(0.05 / max(ms_per_launch * 1e-3, 1e-6)))
+        t0 = time.perf_counter()
+        th = threading.Thread(target=sampler, args=(t0,))
+        th.start()
+        try:
+            while time.perf_counter() - t0 < seconds:
+                for _ in range(batch):
+                    step()
+                torch.cuda.synchronize()
+        finally:
+            stop.set()
+            th.join()
+        kept = [xs for t, xs in samples if t >= 1.2 and xs and xs != before]
+        if not kept:
+            return {"error": "the metrics table did not refresh under load", "idle_xcd_mhz": before}
+        means = sorted(sum(xs) / len(xs) for xs in kept)
+        return {"sclk_mhz": round(means[len(means) // 2], 1), "xcd_mhz": kept[-1], "samples": len(kept),
+                "method": "management library, mean over the XCDs of each one's current graphics clock, "
+                          f"sampled every 20 ms during {seconds:.0f} s of the same launches after the timed region"}
+    except Exception as ex:  # noqa: BLE001 - reported, never fatal
+        return {"error": f"{type(ex).__name__}: {ex}"}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:  # noqa: BLE001
+            pass
+
+
 def two_sided_pairs(N: int, left: int, right: int) -> int:
     """sum_i |S_i| of the two-sided band: min(i, left) + min(N-1-i, right) + 1."""
     return sum(min(i, left) + min(N - 1 - i, right) + 1 for i in range(N))
@@ -539,7 +619,14 @@ def main():
         parity = dict(abs_error(out, want), against="float64 oracle, every output element",
                       bound_max=1.5e-2, bound_mean=1e-3)
         del want
-    clk = {"sclk_mhz": None, "error": "not measured"} if args.no_clock else clock_under_load(step, torch, ms)
+    if args.no_clock:
+        clk = {"sclk_mhz": None, "error": "not measured"}
+    else:
+        # the management library's per-XCD clocks when it is there; the
+        # cycle-counter spin beside it (it has read low under this load)
+        spin = clock_under_load(step, torch, ms)
+        smi = smi_clock_under_load(step, torch, ms)
+        clk = dict(smi, spin=spin) if smi.get("sclk_mhz") else dict(spin, smi=smi or None)
     traffic = read_traffic(cfg.name)
     roof = {"bound": "mfma", "achieved": round(value, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
